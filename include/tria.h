@@ -1,0 +1,224 @@
+/*
+ * tria.h - C ABI of the TriAttention KV-cache pruning pass on MI355X (gfx950).
+ *
+ * One pruning event is three calls on one HIP stream:
+ *
+ *   tria_score   : score every cached key of every (unit, KV head) with the
+ *                  offset-averaged TriAttention score, z-normalise it per query
+ *                  head over the droppable slots and aggregate each GQA group
+ *                  onto its KV head;
+ *   tria_select  : keep the top-B slots per (unit, KV head), sinks and the
+ *                  recent window always included;
+ *   tria_compact : gather the kept K rows, V rows and positions into the
+ *                  destination cache.
+ *
+ * A "unit" is one (layer, sequence) pair; units are independent.  Sources of
+ * the arithmetic (cited by page title and equation):
+ *   - Fold note: academ.us article 2607.13051 (restates the TriAttention score,
+ *     Eqs. 1-3, and folds its future-offset average, Eqs. 4-8);
+ *   - Blog: "TriAttention, or: what a rotating query already knows" (The Method);
+ *   - Calib issue: GitHub issue "Request: publish TriAttention calibration
+ *     script (TRIA v2/v3 stats.bin producer)" (pairing conventions, statistics
+ *     layout, the port's runtime parameters budget / window / sink).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked [device] are device memory owned by the caller; the
+ *     library keeps no pointer after a call returns.  Pointers marked [host]
+ *     are read during the call only.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No entry point synchronises, allocates device memory or copies
+ *     between host and device, except tria_device_flags and the timing calls.
+ *   - Every argument the host can see is validated before anything is
+ *     enqueued: a non-OK status means nothing was launched.  Values that live
+ *     in device memory (lengths, layers, budgets, block ids) cannot be checked
+ *     on the host; the kernels clamp them to safe ranges (no access ever leaves
+ *     the caller's buffers) and record the violation in the workspace's flag
+ *     word, which tria_device_flags reads.
+ *   - Keys and values are bf16 rows of head_dim elements, each row contiguous
+ *     and 16-byte aligned.
+ *   - Entry points are reentrant; calls that share a workspace must not overlap
+ *     in time (use one stream, or one workspace per stream).
+ */
+#ifndef TRIA_H_
+#define TRIA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tria_status {
+  TRIA_OK = 0,
+  TRIA_EINVAL = 1,      /* null pointer, unknown enum value, negative count   */
+  TRIA_ESHAPE = 2,      /* unsupported head_dim / group, inconsistent sizes,
+                           strides or alignment                                */
+  TRIA_EBUDGET = 3,     /* (device flag) a budget below sink + window while
+                           the unit holds more than `budget` keys              */
+  TRIA_EOVERLAP = 4,    /* dense destination range overlaps the source range  */
+  TRIA_EWORKSPACE = 5,  /* workspace missing or smaller than tria_workspace_size */
+  TRIA_ELAUNCH = 6      /* a HIP call failed; tria_last_error() has the detail */
+} tria_status;
+
+/* Band pairing of a head's dims into complex numbers [Calib issue]:
+ *   NEOX        : band f = dim f + i * dim (f + d/2)
+ *   INTERLEAVED : band f = dim 2f + i * dim (2f + 1)                          */
+typedef enum { TRIA_PAIR_NEOX = 0, TRIA_PAIR_INTERLEAVED = 1 } tria_pairing;
+
+/* GQA aggregation of a group's z-scores onto its KV head [Fold note, sec. 4:
+ * "normalize-then-max"; the mean is the other variant].                        */
+typedef enum { TRIA_AGG_MEAN = 0, TRIA_AGG_MAX = 1 } tria_agg;
+
+/* Device-side contract violations, OR-ed into the workspace flag word.        */
+enum {
+  TRIA_FLAG_LEN = 1,     /* len[u] < 0 or > n_max: clamped                     */
+  TRIA_FLAG_LAYER = 2,   /* unit_layer[u] outside [0, n_layers): unit skipped  */
+  TRIA_FLAG_BUDGET = 4,  /* budget[u] < 0, or < min(len, sink + window) while
+                            len > budget: the top-B rule is still applied     */
+  TRIA_FLAG_BLOCK = 8,   /* block id outside [0, n_pool_blocks): row skipped   */
+  TRIA_FLAG_INDEX = 16,  /* compaction index outside [0, len[u]): row skipped  */
+  TRIA_FLAG_BMAX = 32    /* min(budget, len) > b_max: clamped to b_max         */
+};
+
+/* Shape and method parameters (a host struct, read during the call only). */
+typedef struct tria_params {
+  int32_t head_dim;        /* d: 64, 128 or 256                                 */
+  int32_t n_kv_heads;      /* Hkv >= 1                                          */
+  int32_t group;           /* G = query heads per KV head, 1..8; query head h
+                              belongs to KV head h / G                          */
+  int32_t n_layers;        /* L: leading extent of the statistics arrays        */
+  int32_t pairing;         /* tria_pairing                                      */
+  int32_t agg;             /* tria_agg                                          */
+  double rope_base;        /* theta > 1: band f turns at theta^(-2f/d) rad per
+                              position [Fold note, Eq. 2]                       */
+  const int64_t* offsets;  /* [host] future offsets D, each in [0, 2^40]; the
+                              score is averaged over them [Fold note, Eq. 4]    */
+  int32_t n_offsets;       /* |D|, 1..256                                       */
+  int32_t sink;            /* S0 >= 0: the first S0 slots are always kept       */
+  int32_t window;          /* W >= 0: the last W slots are always kept          */
+} tria_params;
+
+/* A K or V cache.  Row of (unit u, KV head g, slot i) starts at element
+ *   dense : base + u*stride_unit + g*stride_head + i*stride_slot
+ *   paged : base + (bt[u*max_blocks + i/block_size]*block_size + i%block_size)
+ *                  * stride_slot + g*stride_head
+ * (strides in bf16 elements, each a multiple of 8; base 16-byte aligned).  */
+typedef struct tria_kv_view {
+  void* base;                 /* [device] bf16 rows                             */
+  int64_t stride_unit;        /* dense only                                     */
+  int64_t stride_head;
+  int64_t stride_slot;
+  const int32_t* block_table; /* [device] [n_units][max_blocks]; NULL = dense   */
+  int32_t block_size;         /* paged: slots per block (>= 1)                  */
+  int32_t max_blocks;         /* paged: row length of block_table               */
+  int64_t n_pool_blocks;      /* paged: blocks in the pool; ids are checked
+                                 against it on the device                       */
+} tria_kv_view;
+
+/* Bytes of workspace tria_score and tria_select need for `n_units` units of at
+ * most `n_max` slots.  With `raw_in_workspace` != 0 the per-query-head scores
+ * are kept in the workspace (tria_score's `raw` may then be NULL).  Returns 0
+ * for invalid parameters. */
+size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max,
+                           int32_t raw_in_workspace);
+
+/* tria_score - the offset-averaged TriAttention score, z-normalised and
+ * aggregated onto each KV head.
+ *
+ * For unit u (layer l = unit_layer[u], n = len[u] cached slots), KV head g and
+ * query head h of g's group, with centre mu_f = q_mean_re + i q_mean_im and
+ * mean magnitude a_f = q_abs_mean of (l, h, f), and key bands k_f read in the
+ * pairing layout and un-rotated at their positions:
+ *   raw[u][h][i] = (1/|D|) sum_{delta in D} sum_f |mu_f||k_f|
+ *                    cos(omega_f (q_pos[u] - p_i + delta) + arg mu_f - arg k_f)
+ *                + sum_f (a_f - |mu_f|) |k_f|
+ * [Fold note, Eqs. 1, 2, 4; the norm term is the reading E|q_f| (1 - R_f) |k_f|
+ * of Blog, The Method].  The kernels evaluate it in the folded form of Eq. 7
+ * with the inverse rotation absorbed by angle addition, so key positions are
+ * not needed: only q_pos.
+ * Then, over the droppable slots C = [sink, n - window) (the candidates):
+ *   z_h(i)     = (raw[u][h][i] - mean_C) / max(std_C, 1e-12)   (population std)
+ *   agg[u][g][i] = mean_h z_h(i)  or  max_h z_h(i)   (per p->agg)
+ * and agg = +inf on the protected slots [0, sink) and [n - window, n).
+ *
+ *   k           [device] K cache view (dense or paged)
+ *   n_units     U >= 0; n_max >= every len[u] (row length of raw and agg)
+ *   len         [device] int32 [U] cached slots per unit
+ *   unit_layer  [device] int32 [U] layer of each unit (row of the statistics)
+ *   q_pos       [device] int32 [U] position of the current query (the newest
+ *               key); future queries sit at q_pos + delta
+ *   q_mean_re, q_mean_im, q_abs_mean
+ *               [device] fp32 [L][G*Hkv][d/2] calibrated query statistics
+ *               E[Re q_f], E[Im q_f], E|q_f| [Calib issue]
+ *   raw         [device] fp32 [U][G*Hkv][n_max] per-query-head scores, or NULL
+ *               (then the workspace must have been sized with raw_in_workspace)
+ *   agg         [device] fp32 [U][Hkv][n_max] aggregated scores; slots >= len[u]
+ *               are left untouched
+ *   ws          [device] workspace of ws_bytes >= tria_workspace_size(...)
+ */
+tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
+                       const int32_t* len, const int32_t* unit_layer, const int32_t* q_pos,
+                       const float* q_mean_re, const float* q_mean_im, const float* q_abs_mean,
+                       float* raw, float* agg, void* ws, size_t ws_bytes, void* stream);
+
+/* tria_select - keep the top-B slots of each (unit, KV head)
+ * ("Sort. Keep the top-B. Drop the rest." [Blog, The Method]).
+ *
+ * Keeps K_u = min(budget[u], len[u]) slots per (u, g): the slots with the
+ * largest agg (protected slots carry +inf, so they are kept whenever
+ * budget >= sink + window); among equal agg the lower slot wins.
+ *   idx  [device] int32 [U][Hkv][b_max]: kept slots in ascending order in
+ *        [0, K_u), -1 in [K_u, b_max)
+ *   cnt  [device] int32 [U]: K_u
+ * b_max must be >= every K_u (else TRIA_FLAG_BMAX and the keep count is
+ * clamped to b_max).
+ */
+tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, int32_t b_max,
+                        const int32_t* len, const int32_t* budget, const float* agg,
+                        int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes, void* stream);
+
+/* tria_compact - gather the kept rows (a bit copy; no conversion).
+ *
+ * For every unit u, KV head g and j < cnt[u], with i = idx[u][g][j]:
+ *   row (u, g, j) of k_dst = row (u, g, i) of k_src;   likewise V;
+ *   pos_dst[u][g][j]       = pos_src[u][g or 0][i].
+ * k_dst / v_dst address kept slot j like a cache of b_max slots (dense) or
+ * through their own block tables (paged).  Out of place only: dense
+ * destinations overlapping the source return TRIA_EOVERLAP; for paged views,
+ * disjoint source and destination blocks are a precondition.
+ *   pos_src   [device] int32 [U][pos_heads][n_max] or NULL (then pos_dst is
+ *             ignored); pos_heads is 1 (shared by all KV heads) or Hkv
+ *   pos_dst   [device] int32 [U][Hkv][b_max] or NULL
+ *   len       [device] int32 [U] (indices are checked against it)
+ */
+tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const tria_kv_view* v_src,
+                         const int32_t* pos_src, int32_t pos_heads, int32_t n_units, int32_t n_max,
+                         int32_t b_max, const int32_t* len, const int32_t* idx, const int32_t* cnt,
+                         const tria_kv_view* k_dst, const tria_kv_view* v_dst, int32_t* pos_dst,
+                         void* stream);
+
+/* Reads (after synchronising `stream`) and clears the device flag word of a
+ * workspace.  Returns TRIA_OK and the OR of TRIA_FLAG_* in *flags. */
+tria_status tria_device_flags(void* ws, int32_t* flags, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* tria_strerror(tria_status s);
+
+/* Detail of the last TRIA_ELAUNCH or validation failure on this thread. */
+const char* tria_last_error(void);
+
+/* Kernel timing with HIP events recorded on the launch stream around every
+ * kernel launch.  tria_timing_enable(1) starts recording (0 stops);
+ * tria_timing_read synchronises on the recorded events and returns, for each
+ * kernel id k < n (see tria_kernel_name), the summed milliseconds and the
+ * number of launches since the last read.  Returns the number of kernel ids. */
+int32_t tria_timing_enable(int32_t on);
+int32_t tria_timing_read(double* ms_sum, int64_t* launches, int32_t n);
+const char* tria_kernel_name(int32_t k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRIA_H_ */

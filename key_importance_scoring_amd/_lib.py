@@ -1,0 +1,171 @@
+"""ctypes binding of libtria.so (include/tria.h).  Argument marshalling only.
+
+Every function has the name and argument order of its C entry point.  Device
+buffers may be passed as torch tensors (their ``data_ptr()`` is used) or as raw
+integer addresses; ``stream`` is a HIP stream handle (an int; 0 = null stream)
+or a ``torch.cuda.Stream``.  A non-OK status raises ``TriaError``.  The library
+must have been built (``python -m key_importance_scoring_amd.build``): there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtria.so")
+
+TRIA_OK, TRIA_EINVAL, TRIA_ESHAPE, TRIA_EBUDGET, TRIA_EOVERLAP, TRIA_EWORKSPACE, TRIA_ELAUNCH = range(7)
+PAIR_NEOX, PAIR_INTERLEAVED = 0, 1
+AGG_MEAN, AGG_MAX = 0, 1
+FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX = 1, 2, 4, 8, 16, 32
+
+EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
+           "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name")
+
+
+class TriaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"tria status {status}: {message}")
+        self.status = status
+
+
+class TriaParams(ctypes.Structure):
+    _fields_ = [("head_dim", c_int32), ("n_kv_heads", c_int32), ("group", c_int32), ("n_layers", c_int32),
+                ("pairing", c_int32), ("agg", c_int32), ("rope_base", c_double),
+                ("offsets", POINTER(c_int64)), ("n_offsets", c_int32), ("sink", c_int32), ("window", c_int32)]
+
+
+class TriaKvView(ctypes.Structure):
+    _fields_ = [("base", c_void_p), ("stride_unit", c_int64), ("stride_head", c_int64), ("stride_slot", c_int64),
+                ("block_table", c_void_p), ("block_size", c_int32), ("max_blocks", c_int32),
+                ("n_pool_blocks", c_int64)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libtria.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m key_importance_scoring_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.tria_workspace_size.restype = c_size_t
+    lib.tria_workspace_size.argtypes = [POINTER(TriaParams), c_int32, c_int32, c_int32]
+    lib.tria_score.restype = c_int32
+    lib.tria_score.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), c_int32, c_int32,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.tria_select.restype = c_int32
+    lib.tria_select.argtypes = [POINTER(TriaParams), c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.tria_compact.restype = c_int32
+    lib.tria_compact.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_void_p, c_int32,
+                                 c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                 POINTER(TriaKvView), POINTER(TriaKvView), c_void_p, c_void_p]
+    lib.tria_device_flags.restype = c_int32
+    lib.tria_device_flags.argtypes = [c_void_p, POINTER(c_int32), c_void_p]
+    lib.tria_strerror.restype = c_char_p
+    lib.tria_strerror.argtypes = [c_int32]
+    lib.tria_last_error.restype = c_char_p
+    lib.tria_last_error.argtypes = []
+    lib.tria_timing_enable.restype = c_int32
+    lib.tria_timing_enable.argtypes = [c_int32]
+    lib.tria_timing_read.restype = c_int32
+    lib.tria_timing_read.argtypes = [POINTER(c_double), POINTER(c_int64), c_int32]
+    lib.tria_kernel_name.restype = c_char_p
+    lib.tria_kernel_name.argtypes = [c_int32]
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------- marshalling helpers
+
+def ptr(x) -> int | None:
+    """Device address of a tensor (or an int address); None stays NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def stream_handle(stream) -> int | None:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_params(head_dim: int, n_kv_heads: int, group: int, n_layers: int, pairing: int, agg: int,
+                rope_base: float, offsets, sink: int, window: int) -> TriaParams:
+    """A TriaParams; the offsets array is kept alive on the returned object."""
+    arr = (c_int64 * len(offsets))(*[int(o) for o in offsets])
+    p = TriaParams(head_dim, n_kv_heads, group, n_layers, pairing, agg, float(rope_base),
+                   ctypes.cast(arr, POINTER(c_int64)), len(offsets), sink, window)
+    p._offsets_keepalive = arr
+    return p
+
+
+def make_view(base, stride_unit: int, stride_head: int, stride_slot: int, block_table=None,
+              block_size: int = 0, max_blocks: int = 0, n_pool_blocks: int = 0) -> TriaKvView:
+    return TriaKvView(ptr(base), stride_unit, stride_head, stride_slot, ptr(block_table),
+                      block_size, max_blocks, n_pool_blocks)
+
+
+def _check(status: int) -> None:
+    if status != TRIA_OK:
+        lib = load()
+        msg = lib.tria_last_error().decode(errors="replace")
+        raise TriaError(status, f"{lib.tria_strerror(status).decode()}: {msg}")
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def tria_workspace_size(p: TriaParams, n_units: int, n_max: int, raw_in_workspace: bool) -> int:
+    return int(load().tria_workspace_size(ctypes.byref(p), n_units, n_max, int(bool(raw_in_workspace))))
+
+
+def tria_score(p: TriaParams, k: TriaKvView, n_units: int, n_max: int, len_, unit_layer, q_pos,
+               q_mean_re, q_mean_im, q_abs_mean, raw, agg, ws, ws_bytes: int, stream=None) -> None:
+    _check(load().tria_score(ctypes.byref(p), ctypes.byref(k), n_units, n_max, ptr(len_), ptr(unit_layer),
+                             ptr(q_pos), ptr(q_mean_re), ptr(q_mean_im), ptr(q_abs_mean), ptr(raw), ptr(agg),
+                             ptr(ws), ws_bytes, stream_handle(stream)))
+
+
+def tria_select(p: TriaParams, n_units: int, n_max: int, b_max: int, len_, budget, agg, idx, cnt,
+                ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(load().tria_select(ctypes.byref(p), n_units, n_max, b_max, ptr(len_), ptr(budget), ptr(agg),
+                              ptr(idx), ptr(cnt), ptr(ws), ws_bytes, stream_handle(stream)))
+
+
+def tria_compact(p: TriaParams, k_src: TriaKvView, v_src: TriaKvView, pos_src, pos_heads: int, n_units: int,
+                 n_max: int, b_max: int, len_, idx, cnt, k_dst: TriaKvView, v_dst: TriaKvView, pos_dst,
+                 stream=None) -> None:
+    _check(load().tria_compact(ctypes.byref(p), ctypes.byref(k_src), ctypes.byref(v_src), ptr(pos_src), pos_heads,
+                               n_units, n_max, b_max, ptr(len_), ptr(idx), ptr(cnt), ctypes.byref(k_dst),
+                               ctypes.byref(v_dst), ptr(pos_dst), stream_handle(stream)))
+
+
+def tria_device_flags(ws, stream=None) -> int:
+    out = c_int32(0)
+    _check(load().tria_device_flags(ptr(ws), ctypes.byref(out), stream_handle(stream)))
+    return int(out.value)
+
+
+def tria_timing_enable(on: bool) -> int:
+    return int(load().tria_timing_enable(int(bool(on))))
+
+
+def tria_timing_read() -> dict:
+    """{kernel name: (summed ms, launches)} since the previous read."""
+    lib = load()
+    n = 16
+    ms = (c_double * n)()
+    cnt = (c_int64 * n)()
+    k = int(lib.tria_timing_read(ms, cnt, n))
+    return {lib.tria_kernel_name(i).decode(): (ms[i], int(cnt[i])) for i in range(k)}

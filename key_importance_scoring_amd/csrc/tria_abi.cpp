@@ -1,0 +1,342 @@
+// C ABI of the TriAttention pruning pass (declared in include/tria.h):
+// host-side validation, workspace layout, launch sequencing and kernel timing.
+// All arithmetic of the pass runs in the kernels of tria_kernels.hip.
+#include "tria.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "tria_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tria_status fail(tria_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// ------------------------------------------------------------------ timing
+enum { kIdCoef = 0, kIdScore, kIdAgg, kIdSelect, kIdCompact, kNumIds };
+const char* const kNames[kNumIds] = {"k_coef", "k_score", "k_agg", "k_select", "k_compact"};
+
+struct Rec {
+  int id;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<Rec> g_recs;
+
+// Runs `launch` on `stream`, bracketed by HIP events on the same stream when
+// timing is on.
+template <class Fn>
+hipError_t timed(int id, hipStream_t stream, Fn&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    on = g_timing;
+  }
+  if (!on) return launch();
+  Rec r{id, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&r.a);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&r.b);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(r.a, stream)) != hipSuccess) return e;
+  if ((e = launch()) != hipSuccess) return e;
+  if ((e = hipEventRecord(r.b, stream)) != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_recs.push_back(r);
+  return hipSuccess;
+}
+
+tria_status launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TRIA_OK;
+  return fail(TRIA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------------ validation
+tria_status check_params(const tria_params* p) {
+  if (!p) return fail(TRIA_EINVAL, "params is NULL");
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(TRIA_ESHAPE, "head_dim %d not in {64, 128, 256}", p->head_dim);
+  if (p->n_kv_heads < 1) return fail(TRIA_ESHAPE, "n_kv_heads %d < 1", p->n_kv_heads);
+  if (p->group < 1 || p->group > tria::kMaxGroup)
+    return fail(TRIA_ESHAPE, "group %d not in [1, %d]", p->group, tria::kMaxGroup);
+  if (p->n_layers < 1) return fail(TRIA_ESHAPE, "n_layers %d < 1", p->n_layers);
+  if (p->pairing != TRIA_PAIR_NEOX && p->pairing != TRIA_PAIR_INTERLEAVED)
+    return fail(TRIA_EINVAL, "unknown pairing %d", p->pairing);
+  if (p->agg != TRIA_AGG_MEAN && p->agg != TRIA_AGG_MAX) return fail(TRIA_EINVAL, "unknown agg %d", p->agg);
+  if (!(p->rope_base > 1.0) || !std::isfinite(p->rope_base))
+    return fail(TRIA_EINVAL, "rope_base must be a finite value > 1");
+  if (!p->offsets) return fail(TRIA_EINVAL, "offsets is NULL");
+  if (p->n_offsets < 1 || p->n_offsets > tria::kMaxOffsets)
+    return fail(TRIA_EINVAL, "n_offsets %d not in [1, %d]", p->n_offsets, tria::kMaxOffsets);
+  for (int i = 0; i < p->n_offsets; ++i)
+    if (p->offsets[i] < 0 || p->offsets[i] > (int64_t(1) << 40))
+      return fail(TRIA_EINVAL, "offset[%d] = %lld outside [0, 2^40]", i, (long long)p->offsets[i]);
+  if (p->sink < 0 || p->window < 0) return fail(TRIA_EINVAL, "sink and window must be >= 0");
+  return TRIA_OK;
+}
+
+tria_status check_view(const tria_kv_view* v, const char* name, int head_dim, int32_t n_slots) {
+  if (!v) return fail(TRIA_EINVAL, "%s view is NULL", name);
+  if (!v->base) return fail(TRIA_EINVAL, "%s base is NULL", name);
+  if (reinterpret_cast<uintptr_t>(v->base) % 16 != 0) return fail(TRIA_ESHAPE, "%s base not 16-byte aligned", name);
+  if (v->stride_head < 0 || v->stride_slot < 0 || v->stride_unit < 0)
+    return fail(TRIA_ESHAPE, "%s has a negative stride", name);
+  if (v->stride_head % 8 || v->stride_slot % 8 || v->stride_unit % 8)
+    return fail(TRIA_ESHAPE, "%s strides must be multiples of 8 elements", name);
+  if (v->block_table) {
+    if (v->block_size < 1 || v->max_blocks < 1 || v->n_pool_blocks < 1)
+      return fail(TRIA_ESHAPE, "%s: paged view needs block_size, max_blocks, n_pool_blocks >= 1", name);
+    if ((int64_t)v->max_blocks * v->block_size < n_slots)
+      return fail(TRIA_ESHAPE, "%s: block table covers %lld slots < %d", name,
+                  (long long)v->max_blocks * v->block_size, n_slots);
+  }
+  (void)head_dim;
+  return TRIA_OK;
+}
+
+tria::KView kview(const tria_kv_view* v) {
+  return tria::KView{static_cast<const uint16_t*>(v->base), v->stride_unit, v->stride_head, v->stride_slot,
+                     v->block_table, v->block_size, v->max_blocks, v->n_pool_blocks};
+}
+
+tria::MutKView mkview(const tria_kv_view* v) {
+  return tria::MutKView{static_cast<uint16_t*>(v->base), v->stride_unit, v->stride_head, v->stride_slot,
+                        v->block_table, v->block_size, v->max_blocks, v->n_pool_blocks};
+}
+
+// Byte interval [lo, hi) covered by a dense view of `units` x Hkv x `slots` rows.
+void dense_range(const tria_kv_view* v, int32_t units, int32_t hkv, int32_t slots, int d, uintptr_t& lo,
+                 uintptr_t& hi) {
+  lo = reinterpret_cast<uintptr_t>(v->base);
+  const int64_t last = (int64_t)(units - 1) * v->stride_unit + (int64_t)(hkv - 1) * v->stride_head +
+                       (int64_t)(slots - 1) * v->stride_slot + d;
+  hi = lo + 2 * (uintptr_t)last;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+// ------------------------------------------------------------------ workspace
+struct Layout {
+  size_t C, N, part, raw, total;
+  int32_t n_tiles;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout layout(const tria_params* p, int32_t n_units, int32_t n_max, bool raw_ws) {
+  Layout L{};
+  const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
+  L.n_tiles = (n_max + tria::kScoreTile - 1) / tria::kScoreTile;
+  size_t off = 256;  // flag word
+  L.C = off;
+  off += al256(U * hq * d * 4);
+  L.N = off;
+  off += al256(U * hq * (d / 2) * 4);
+  L.part = off;
+  off += al256(U * hq * (size_t)L.n_tiles * 3 * 8);
+  L.raw = off;
+  if (raw_ws) off += al256(U * hq * (size_t)n_max * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max, int32_t raw_in_workspace) {
+  if (check_params(p) != TRIA_OK || n_units < 0 || n_max < 0) return 0;
+  return layout(p, n_units, n_max, raw_in_workspace != 0).total;
+}
+
+tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
+                       const int32_t* len, const int32_t* unit_layer, const int32_t* q_pos,
+                       const float* q_mean_re, const float* q_mean_im, const float* q_abs_mean, float* raw,
+                       float* agg, void* ws, size_t ws_bytes, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_units < 0 || n_max < 0) return fail(TRIA_EINVAL, "n_units and n_max must be >= 0");
+  if (n_max % 16 != 0) return fail(TRIA_ESHAPE, "n_max %d must be a multiple of 16", n_max);
+  if ((st = check_view(k, "k", p->head_dim, n_max)) != TRIA_OK) return st;
+  if (!len || !unit_layer || !q_pos || !q_mean_re || !q_mean_im || !q_abs_mean || !agg)
+    return fail(TRIA_EINVAL, "a required device pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(agg) % 16 || (raw && reinterpret_cast<uintptr_t>(raw) % 16))
+    return fail(TRIA_ESHAPE, "raw and agg must be 16-byte aligned");
+  if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(TRIA_EWORKSPACE, "workspace must be 256-byte aligned");
+  const Layout L = layout(p, n_units, n_max, raw == nullptr);
+  if (ws_bytes < L.total)
+    return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if (n_units == 0 || n_max == 0) return TRIA_OK;
+
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* flags = reinterpret_cast<int32_t*>(w);
+  float* C = reinterpret_cast<float*>(w + L.C);
+  float* N = reinterpret_cast<float*>(w + L.N);
+  double* part = reinterpret_cast<double*>(w + L.part);
+  float* rawp = raw ? raw : reinterpret_cast<float*>(w + L.raw);
+
+  tria::Offsets offs{};
+  offs.n = p->n_offsets;
+  for (int i = 0; i < p->n_offsets; ++i) offs.v[i] = (double)p->offsets[i];
+
+  tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->head_dim, p->n_layers, p->pairing, std::log(p->rope_base),
+                    len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, C, N, flags};
+  hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
+  if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
+
+  tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window, L.n_tiles,
+                     len, C, N, rawp, part, flags};
+  e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, s); });
+  if ((st = launch_status(e, "k_score")) != TRIA_OK) return st;
+
+  tria::AggArgs aa{n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window, L.n_tiles,
+                   (n_max + tria::kAggTile - 1) / tria::kAggTile, p->agg, len, rawp, part, agg};
+  e = timed(kIdAgg, s, [&] { return tria::launch_agg(aa, s); });
+  return launch_status(e, "k_agg");
+}
+
+tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+                        const int32_t* budget, const float* agg, int32_t* idx, int32_t* cnt, void* ws,
+                        size_t ws_bytes, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
+  if (!len || !budget || !agg || !idx || !cnt) return fail(TRIA_EINVAL, "a required device pointer is NULL");
+  if (ws && ws_bytes < 256) return fail(TRIA_EWORKSPACE, "workspace %zu bytes < 256", ws_bytes);
+  if (n_units == 0) return TRIA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, len, budget, agg, idx, cnt,
+                      static_cast<int32_t*>(ws)};
+  hipError_t e = timed(kIdSelect, s, [&] { return tria::launch_select(sa, s); });
+  return launch_status(e, "k_select");
+}
+
+tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const tria_kv_view* v_src,
+                         const int32_t* pos_src, int32_t pos_heads, int32_t n_units, int32_t n_max, int32_t b_max,
+                         const int32_t* len, const int32_t* idx, const int32_t* cnt, const tria_kv_view* k_dst,
+                         const tria_kv_view* v_dst, int32_t* pos_dst, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
+  if ((st = check_view(k_src, "k_src", p->head_dim, n_max)) != TRIA_OK) return st;
+  if ((st = check_view(v_src, "v_src", p->head_dim, n_max)) != TRIA_OK) return st;
+  if ((st = check_view(k_dst, "k_dst", p->head_dim, b_max)) != TRIA_OK) return st;
+  if ((st = check_view(v_dst, "v_dst", p->head_dim, b_max)) != TRIA_OK) return st;
+  if (!len || !idx || !cnt) return fail(TRIA_EINVAL, "a required device pointer is NULL");
+  if (pos_src && pos_heads != 1 && pos_heads != p->n_kv_heads)
+    return fail(TRIA_ESHAPE, "pos_heads %d must be 1 or n_kv_heads", pos_heads);
+  if (n_units == 0 || b_max == 0) return TRIA_OK;
+
+  // out of place only: dense destinations must not overlap any source
+  const int hkv = p->n_kv_heads, d = p->head_dim;
+  const tria_kv_view* srcs[2] = {k_src, v_src};
+  const tria_kv_view* dsts[2] = {k_dst, v_dst};
+  for (const tria_kv_view* dv : dsts) {
+    if (dv->block_table) continue;
+    uintptr_t d0, d1;
+    dense_range(dv, n_units, hkv, b_max, d, d0, d1);
+    for (const tria_kv_view* sv : srcs) {
+      if (sv->block_table) continue;
+      uintptr_t s0, s1;
+      dense_range(sv, n_units, hkv, n_max, d, s0, s1);
+      if (overlaps(d0, d1, s0, s1)) return fail(TRIA_EOVERLAP, "dense destination overlaps a source cache");
+    }
+  }
+  if (!k_dst->block_table && !v_dst->block_table) {
+    uintptr_t a0, a1, b0, b1;
+    dense_range(k_dst, n_units, hkv, b_max, d, a0, a1);
+    dense_range(v_dst, n_units, hkv, b_max, d, b0, b1);
+    if (overlaps(a0, a1, b0, b1)) return fail(TRIA_EOVERLAP, "k_dst and v_dst overlap");
+  }
+  if (pos_src && pos_dst) {
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(pos_src);
+    const uintptr_t s1 = s0 + (size_t)n_units * pos_heads * n_max * 4;
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(pos_dst);
+    const uintptr_t d1 = d0 + (size_t)n_units * hkv * b_max * 4;
+    if (overlaps(s0, s1, d0, d1)) return fail(TRIA_EOVERLAP, "pos_dst overlaps pos_src");
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t n_rtiles = (b_max + tria::kCompactRows - 1) / tria::kCompactRows;
+  tria::CompactArgs ca{kview(k_src), kview(v_src), mkview(k_dst), mkview(v_dst), pos_src, pos_heads, pos_dst,
+                       n_units, n_max, b_max, hkv, d, n_rtiles, len, idx, cnt, nullptr};
+  hipError_t e = timed(kIdCompact, s, [&] { return tria::launch_compact(ca, s); });
+  return launch_status(e, "k_compact");
+}
+
+tria_status tria_device_flags(void* ws, int32_t* flags, void* stream) {
+  if (!ws || !flags) return fail(TRIA_EINVAL, "ws and flags must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemsetAsync(ws, 0, sizeof v, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(TRIA_ELAUNCH, "tria_device_flags: %s", hipGetErrorString(e));
+  *flags = v;
+  return TRIA_OK;
+}
+
+const char* tria_strerror(tria_status s) {
+  switch (s) {
+    case TRIA_OK: return "ok";
+    case TRIA_EINVAL: return "invalid argument";
+    case TRIA_ESHAPE: return "unsupported or inconsistent shape";
+    case TRIA_EBUDGET: return "budget below the protected slots";
+    case TRIA_EOVERLAP: return "destination overlaps source";
+    case TRIA_EWORKSPACE: return "workspace missing or too small";
+    case TRIA_ELAUNCH: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* tria_last_error(void) { return g_err; }
+
+int32_t tria_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return kNumIds;
+}
+
+int32_t tria_timing_read(double* ms_sum, int64_t* launches, int32_t n) {
+  std::vector<Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs.swap(g_recs);
+  }
+  for (int i = 0; i < n && i < kNumIds; ++i) {
+    if (ms_sum) ms_sum[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (const Rec& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess && r.id < n) {
+      if (ms_sum) ms_sum[r.id] += ms;
+      if (launches) launches[r.id] += 1;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  return kNumIds;
+}
+
+const char* tria_kernel_name(int32_t k) { return (k >= 0 && k < kNumIds) ? kNames[k] : ""; }
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal interface between the C ABI (tria_abi.cpp) and the gfx950 kernels
+// (tria_kernels.hip).  Not installed; the public interface is include/tria.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tria {
+
+constexpr int kMaxOffsets = 256;
+constexpr int kMaxGroup = 8;
+constexpr int kScoreTile = 2048;   // keys per score workgroup
+constexpr int kAggTile = 1024;     // keys per z-norm/GQA workgroup
+constexpr int kSelectThreads = 1024;
+
+// A cache view with element strides (bf16 elements).
+struct KView {
+  const uint16_t* base;
+  int64_t su, sh, ss;
+  const int32_t* bt;   // nullptr: dense
+  int32_t bs, mb;
+  int64_t npb;
+};
+
+struct MutKView {
+  uint16_t* base;
+  int64_t su, sh, ss;
+  const int32_t* bt;
+  int32_t bs, mb;
+  int64_t npb;
+};
+
+struct Offsets {
+  double v[kMaxOffsets];
+  int32_t n;
+};
+
+struct CoefArgs {
+  int32_t n_units, hq, d, layers, pairing;
+  double log_base;            // ln(theta)
+  const int32_t* len;
+  const int32_t* unit_layer;
+  const int32_t* q_pos;
+  const float* q_re;
+  const float* q_im;
+  const float* q_abs;
+  float* C;                   // [U][Hq][d]
+  float* N;                   // [U][Hq][d/2]
+  int32_t* flags;
+};
+
+struct ScoreArgs {
+  KView k;
+  int32_t n_units, n_max, hkv, group, sink, window, n_tiles;
+  const int32_t* len;
+  const float* C;
+  const float* N;
+  float* raw;                 // [U][Hq][n_max]
+  double* part;               // [U][Hq][n_tiles][3]
+  int32_t* flags;
+};
+
+struct AggArgs {
+  int32_t n_units, n_max, hkv, group, sink, window, n_tiles, n_atiles, agg;
+  const int32_t* len;
+  const float* raw;
+  const double* part;
+  float* out;                 // [U][Hkv][n_max]
+};
+
+struct SelectArgs {
+  int32_t n_units, n_max, b_max, hkv, sink, window;
+  const int32_t* len;
+  const int32_t* budget;
+  const float* agg;
+  int32_t* idx;               // [U][Hkv][b_max]
+  int32_t* cnt;               // [U]
+  int32_t* flags;             // may be null
+};
+
+struct CompactArgs {
+  KView ks, vs;
+  MutKView kd, vd;
+  const int32_t* pos_src;
+  int32_t pos_heads;
+  int32_t* pos_dst;
+  int32_t n_units, n_max, b_max, hkv, d, n_rtiles;
+  const int32_t* len;
+  const int32_t* idx;
+  const int32_t* cnt;
+  int32_t* flags;             // may be null
+};
+
+constexpr int kCompactRows = 64;   // kept rows per compaction workgroup
+
+hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s);
+hipError_t launch_agg(const AggArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+}  // namespace tria

@@ -1,0 +1,165 @@
+"""Device-resident workloads for the C-ABI pass.
+
+``DeviceProblem(cfg)`` uploads one synthetic workload (``synth.Config``) to the
+GPU with torch (device memory and streams only), allocates every output and the
+workspace, and runs the three entry points through the binding:
+``score() -> select() -> compact()``.  All arithmetic runs in libtria.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from . import synth
+
+
+def round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+def _bf16(arr: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> a bf16 device tensor with the same bits."""
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def params_for(cfg: synth.Config) -> L.TriaParams:
+    return L.make_params(cfg.head_dim, cfg.n_kv_heads, cfg.group, cfg.n_layers,
+                         L.PAIR_NEOX if cfg.pairing == "neox" else L.PAIR_INTERLEAVED,
+                         L.AGG_MEAN if cfg.agg == "mean" else L.AGG_MAX,
+                         cfg.rope_base, cfg.offsets, cfg.sink, cfg.window)
+
+
+class DeviceProblem:
+    """One workload resident in HBM, plus its outputs and workspace."""
+
+    def __init__(self, cfg: synth.Config, device: str = "cuda:0", keep_raw: bool = True,
+                 workers: int | None = None, k_host: np.ndarray | None = None, v_host: np.ndarray | None = None):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        u = synth.units(cfg)
+        self.units = u
+        U, Hkv, G, d = cfg.n_units, cfg.n_kv_heads, cfg.group, cfg.head_dim
+        self.n_max = round_up(max(u.n_max, 1), 16)
+        self.b_max = max(u.b_max, 1)
+        self.params = params_for(cfg)
+
+        # --- K / V caches
+        if k_host is None:
+            k_host = self._host_cache("k", workers)
+        self.K = _bf16(k_host, self.dev)
+        del k_host
+        if v_host is None:
+            v_host = self._host_cache("v", workers)
+        self.V = _bf16(v_host, self.dev)
+        del v_host
+
+        if cfg.paged:
+            pg = synth.paging(cfg)
+            self.paging = pg
+            self.bt = torch.from_numpy(pg.block_table).to(self.dev)
+            self.dbt = torch.from_numpy(pg.dst_block_table).to(self.dev)
+            bs = cfg.block_size
+            self.k_view = L.make_view(self.K, 0, d, Hkv * d, self.bt, bs, pg.block_table.shape[1], pg.n_blocks)
+            self.v_view = L.make_view(self.V, 0, d, Hkv * d, self.bt, bs, pg.block_table.shape[1], pg.n_blocks)
+            self.K_out = torch.zeros((pg.n_dst_blocks, bs, Hkv, d), dtype=torch.bfloat16, device=self.dev)
+            self.V_out = torch.zeros_like(self.K_out)
+            mdb = pg.dst_block_table.shape[1]
+            self.kd_view = L.make_view(self.K_out, 0, d, Hkv * d, self.dbt, bs, mdb, pg.n_dst_blocks)
+            self.vd_view = L.make_view(self.V_out, 0, d, Hkv * d, self.dbt, bs, mdb, pg.n_dst_blocks)
+        else:
+            self.paging = None
+            nm = self.K.shape[2]
+            self.k_view = L.make_view(self.K, Hkv * nm * d, nm * d, d)
+            self.v_view = L.make_view(self.V, Hkv * nm * d, nm * d, d)
+            self.K_out = torch.zeros((U, Hkv, self.b_max, d), dtype=torch.bfloat16, device=self.dev)
+            self.V_out = torch.zeros_like(self.K_out)
+            self.kd_view = L.make_view(self.K_out, Hkv * self.b_max * d, self.b_max * d, d)
+            self.vd_view = L.make_view(self.V_out, Hkv * self.b_max * d, self.b_max * d, d)
+
+        # --- per-unit metadata and statistics
+        to = lambda a, dt=torch.int32: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev, dt)
+        self.len = to(u.lengths)
+        self.unit_layer = to(u.unit_layer)
+        self.q_pos = to(u.q_pos)
+        self.budget = to(u.budget)
+        re, im, ab = synth.q_stats(cfg)
+        self.q_re, self.q_im, self.q_abs = to(re, torch.float32), to(im, torch.float32), to(ab, torch.float32)
+        pos = synth.positions_all(cfg)
+        pos_pad = np.zeros((U, 1, self.n_max), np.int32)
+        pos_pad[:, 0, :pos.shape[1]] = pos
+        self.pos = to(pos_pad)
+
+        # --- outputs and workspace
+        Hq = cfg.n_q_heads
+        self.raw = torch.zeros((U, Hq, self.n_max), dtype=torch.float32, device=self.dev) if keep_raw else None
+        self.agg = torch.zeros((U, Hkv, self.n_max), dtype=torch.float32, device=self.dev)
+        self.idx = torch.zeros((U, Hkv, self.b_max), dtype=torch.int32, device=self.dev)
+        self.cnt = torch.zeros((U,), dtype=torch.int32, device=self.dev)
+        self.pos_out = torch.zeros((U, Hkv, self.b_max), dtype=torch.int32, device=self.dev)
+        self.ws_bytes = L.tria_workspace_size(self.params, U, self.n_max, self.raw is None)
+        self.ws = torch.zeros((self.ws_bytes,), dtype=torch.uint8, device=self.dev)
+
+    def _host_cache(self, which: str, workers) -> np.ndarray:
+        cfg = self.cfg
+        if cfg.paged:
+            return synth.build_cache(cfg, which, workers)
+        # dense caches padded to n_max slots
+        u = self.units
+        out = np.zeros((cfg.n_units, cfg.n_kv_heads, self.n_max, cfg.head_dim), dtype=np.uint16)
+        for unit, head, rows in synth.iter_chunks(cfg, which, workers):
+            out[unit, head, :rows.shape[0]] = rows
+        del u
+        return out
+
+    # ------------------------------------------------------------------ the pass
+    def score(self, stream=None):
+        L.tria_score(self.params, self.k_view, self.cfg.n_units, self.n_max, self.len, self.unit_layer, self.q_pos,
+                     self.q_re, self.q_im, self.q_abs, self.raw, self.agg, self.ws, self.ws_bytes, stream)
+
+    def select(self, stream=None):
+        L.tria_select(self.params, self.cfg.n_units, self.n_max, self.b_max, self.len, self.budget, self.agg,
+                      self.idx, self.cnt, self.ws, self.ws_bytes, stream)
+
+    def compact(self, idx=None, stream=None):
+        L.tria_compact(self.params, self.k_view, self.v_view, self.pos, 1, self.cfg.n_units, self.n_max,
+                       self.b_max, self.len, self.idx if idx is None else idx, self.cnt, self.kd_view, self.vd_view,
+                       self.pos_out, stream)
+
+    def run(self, stream=None):
+        self.score(stream)
+        self.select(stream)
+        self.compact(stream=stream)
+
+    def flags(self) -> int:
+        return L.tria_device_flags(self.ws, torch.cuda.current_stream(self.dev))
+
+    # ------------------------------------------------------------------ readback helpers
+    def kept(self, unit: int, kv_head: int) -> np.ndarray:
+        k = int(self.cnt[unit].item())
+        return self.idx[unit, kv_head, :k].cpu().numpy().astype(np.int64)
+
+    def out_rows(self, which: str, unit: int, kv_head: int, count: int) -> np.ndarray:
+        """bf16 bits [count][d] of the compacted rows of (unit, kv_head)."""
+        T = self.K_out if which == "k" else self.V_out
+        if not self.cfg.paged:
+            t = T[unit, kv_head, :count]
+        else:
+            bs = self.cfg.block_size
+            bt = torch.from_numpy(self.paging.dst_block_table[unit]).to(self.dev).long()
+            j = torch.arange(count, device=self.dev)
+            t = T[bt[j // bs], j % bs, kv_head]
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the pass must move at minimum: every K row read once, plus the kept K and V
+        rows read and written, plus 4 B read + 4 B written of position per kept row."""
+        cfg, u = self.cfg, self.units
+        row = 2 * cfg.head_dim
+        keys = int(u.lengths.astype(np.int64).sum()) * cfg.n_kv_heads
+        kept = int(np.minimum(u.budget, u.lengths).astype(np.int64).sum()) * cfg.n_kv_heads
+        return keys * row + kept * (4 * row + 8)
+
+    def head_keys(self) -> int:
+        return int(self.units.lengths.astype(np.int64).sum()) * self.cfg.n_kv_heads

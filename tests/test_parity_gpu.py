@@ -1,0 +1,197 @@
+"""GPU parity: the HIP pass (through the C ABI) against the fp64 oracle.
+
+Small cases run every unit and KV head element by element; they span several
+score tiles (2048 keys) with ragged tails, both pairings, head dims 64/128/256,
+mean and max aggregation, paged caches and the degenerate budgets.  The full-size
+workloads run in the same launch configuration as the benchmark and are checked
+on sampled units (every key of each sampled (unit, KV head), since the z-norm and
+the top-B depend on all of them).
+"""
+import numpy as np
+import pytest
+import torch
+
+from _parity import check_compaction, check_kept, check_raw, check_unit, log, oracle_head
+from oracle import tria_oracle as o
+from key_importance_scoring_amd import _lib as L
+from key_importance_scoring_amd import synth
+from key_importance_scoring_amd.device import DeviceProblem
+
+pytestmark = pytest.mark.gpu
+
+C = synth.CONFIGS
+SMALL = {
+    "tiny": C["tiny"],
+    "q8_small": C["qwen3_8b"].replace(name="q8_small", n_layers=2, n_kv=5003, budget=1000),
+    "q32_small": C["qwen3_32b"].replace(name="q32_small", n_layers=3, n_kv=4099, budget=1500, nonconc_frac=0.25),
+    "bd_small": C["batched_decode"].replace(name="bd_small", n_seqs=6, n_kv=3000, ragged_min=300),
+    "lc_small": C["long_context"].replace(name="lc_small", n_kv=6000, budget=600),
+    "d256_neox": C["qwen3_8b"].replace(name="d256_neox", head_dim=256, n_layers=1, n_kv_heads=2, n_kv=2500,
+                                       budget=700),
+    "d256_inter": C["long_context"].replace(name="d256_inter", head_dim=256, n_kv_heads=2, group=3, n_kv=2100,
+                                            budget=900),
+    "d64_inter": C["tiny"].replace(name="d64_inter", pairing="interleaved", n_kv=3001, budget=1200, sink=3,
+                                   agg="max"),
+    "g1_g7": C["qwen3_8b"].replace(name="g1", n_layers=1, n_kv_heads=3, group=1, n_kv=2300, budget=400),
+    "g7": C["qwen3_8b"].replace(name="g7", n_layers=1, n_kv_heads=2, group=7, n_kv=2222, budget=800, agg="mean"),
+    "keep_all": C["tiny"].replace(name="keep_all", n_kv=900, budget=5000),
+    "all_protected": C["tiny"].replace(name="all_protected", n_kv=200, window=256, budget=300),
+    "short_units": C["batched_decode"].replace(name="short_units", n_seqs=5, n_kv=40, ragged_min=1, window=8,
+                                              sink=2, budget_frac=0.5),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+def _run(cfg, **kw):
+    log(f"[parity] {cfg.name}: units={cfg.n_units} Hkv={cfg.n_kv_heads} G={cfg.group} d={cfg.head_dim} "
+        f"n_kv={cfg.n_kv} pairing={cfg.pairing} paged={cfg.paged}")
+    prob = DeviceProblem(cfg, **kw)
+    prob.run()
+    torch.cuda.synchronize()
+    return prob
+
+
+def _oracle_idx(prob, kept_by_unit):
+    """An idx tensor holding the oracle's kept slots (the GPU's elsewhere)."""
+    idx = prob.idx.clone()
+    for unit, per_head in kept_by_unit.items():
+        for g, kept in per_head.items():
+            idx[unit, g, :kept.size] = torch.from_numpy(kept.astype(np.int32)).to(idx.device)
+    return idx
+
+
+def _check_oracle_compaction(prob, kept_by_unit):
+    prob.compact(idx=_oracle_idx(prob, kept_by_unit))
+    torch.cuda.synchronize()
+    for unit, per_head in kept_by_unit.items():
+        for g, kept in per_head.items():
+            check_compaction(prob, unit, g, kept, f"{prob.cfg.name} unit {unit} kv {g} (oracle idx)")
+
+
+def _expected_flags(cfg):
+    """TRIA_FLAG_BUDGET is expected where a budget is below the protected slots of a
+    unit that holds more keys than its budget."""
+    u = synth.units(cfg)
+    prot = np.minimum(u.lengths, cfg.sink + cfg.window)
+    return L.FLAG_BUDGET if bool(((u.lengths > u.budget) & (u.budget < prot)).any()) else 0
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    cfg = SMALL[name]
+    prob = _run(cfg)
+    assert prob.flags() == _expected_flags(cfg)
+    form = "direct" if name == "tiny" else "folded"
+    kept = {unit: check_unit(prob, unit, form=form) for unit in range(cfg.n_units)}
+    _check_oracle_compaction(prob, kept)
+
+
+@pytest.mark.parametrize("name", ["q8_small", "lc_small", "bd_small"])
+def test_small_raw_against_direct_form(name):
+    """The literal 17-offset average, not only the folded oracle."""
+    cfg = SMALL[name]
+    prob = _run(cfg)
+    unit = cfg.n_units - 1
+    g = cfg.n_kv_heads - 1
+    o_raw, _, _ = oracle_head(cfg, unit, g, form="direct")
+    n = int(synth.units(cfg).lengths[unit])
+    check_raw(prob.raw[unit, g * cfg.group:(g + 1) * cfg.group, :n].cpu().numpy(), o_raw, f"{name} direct")
+
+
+def test_zero_statistics_break_ties_by_slot():
+    """All-zero statistics give every key the score 0: the kept candidates must be
+    the lowest slots (ties go to the lower slot)."""
+    cfg = C["tiny"].replace(name="zero_stats", n_kv=3000, budget=900, sink=5, window=100, agg="max")
+    prob = DeviceProblem(cfg)
+    for t in (prob.q_re, prob.q_im, prob.q_abs):
+        t.zero_()
+    prob.run()
+    torch.cuda.synchronize()
+    F = cfg.head_dim // 2
+    zero = np.zeros((cfg.n_layers, cfg.n_q_heads, F))
+    kept = {0: check_unit(prob, 0, mu=zero.astype(complex), absm=zero)}
+    for g in range(cfg.n_kv_heads):
+        want = np.concatenate([np.arange(5), np.arange(5, 5 + 900 - 105), np.arange(2900, 3000)])
+        np.testing.assert_array_equal(prob.kept(0, g), want)
+    _check_oracle_compaction(prob, kept)
+
+
+def test_empty_and_zero_budget_units():
+    cfg = C["batched_decode"].replace(name="empty", n_seqs=4, n_kv=700, ragged_min=100, window=0, sink=0)
+    prob = DeviceProblem(cfg)
+    prob.len[1] = 0
+    prob.budget[2] = 0
+    prob.run()
+    torch.cuda.synchronize()
+    assert prob.flags() == 0
+    cnt = prob.cnt.cpu().numpy()
+    assert cnt[1] == 0 and cnt[2] == 0
+    assert (prob.idx[1].cpu().numpy() == -1).all() and (prob.idx[2].cpu().numpy() == -1).all()
+    for unit in (0, 3):
+        check_unit(prob, unit)
+
+
+def test_device_flags_record_bad_metadata():
+    """Out-of-contract device metadata is clamped by the kernels and reported."""
+    cfg = C["batched_decode"].replace(name="flags", n_seqs=3, n_kv=500, ragged_min=200)
+    prob = DeviceProblem(cfg)
+    prob.len[0] = prob.n_max + 7        # clamped to n_max
+    prob.unit_layer[1] = 5              # no such layer: coefficients are zero
+    prob.budget[2] = 3                  # below sink + window while len > budget
+    prob.run()
+    torch.cuda.synchronize()
+    f = prob.flags()
+    assert f & L.FLAG_LEN and f & L.FLAG_LAYER and f & L.FLAG_BUDGET
+    assert prob.flags() == 0            # reading clears the word
+    assert int(prob.cnt[2].item()) == 3
+
+
+# ----------------------------------------------------------------------------- full sizes
+
+FULL_SAMPLES = {
+    "qwen3_8b": [(0, None), (35, None)],
+    "qwen3_32b": [(0, None), (63, None)],
+    "batched_decode": [(0, None), (37, None), (63, None)],
+    "long_context": [(0, [0, 5, 7])],
+}
+
+
+def _nonconc_unit(cfg):
+    nc = synth.nonconcentrated(cfg)
+    rows = np.nonzero(nc.any(axis=1))[0]
+    return int(rows[0]) if rows.size else 0
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_full_size_sampled_units(name):
+    cfg = C[name]
+    prob = _run(cfg)
+    assert prob.flags() == 0
+    samples = list(FULL_SAMPLES[name])
+    if name == "qwen3_32b":
+        samples.append((_nonconc_unit(cfg), None))
+    kept = {}
+    for unit, heads in samples:
+        log(f"[parity] {name}: checking unit {unit}")
+        kept[unit] = check_unit(prob, unit, heads=heads)
+    # properties that hold for every unit: counts, ranges, protected slots kept
+    u = synth.units(cfg)
+    cnt = prob.cnt.cpu().numpy()
+    np.testing.assert_array_equal(cnt, np.minimum(u.budget, u.lengths))
+    idx = prob.idx.cpu().numpy()
+    for unit in range(cfg.n_units):
+        n = int(u.lengths[unit])
+        k = int(cnt[unit])
+        blk = idx[unit, :, :k]
+        assert (np.diff(blk, axis=1) > 0).all() and (blk >= 0).all() and (blk < n).all()
+        prot = np.nonzero(o.protected_mask(n, cfg.sink, cfg.window))[0]
+        for g in range(cfg.n_kv_heads):
+            assert np.isin(prot, blk[g]).all()
+        assert (idx[unit, :, k:] == -1).all()
+    _check_oracle_compaction(prob, kept)
