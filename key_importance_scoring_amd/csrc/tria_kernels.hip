@@ -176,7 +176,6 @@ struct Shape {
   static constexpr int NKC = D / 32;    // chunks per lane = MFMAs of the dot part
   static constexpr int NQ = D / 8;      // bands per lane
   static constexpr int NNC = D / 64;    // MFMAs per norm part
-  static constexpr int NBI = D >= 256 ? 2 : 4;  // 16-key blocks in flight per wave
 };
 
 template <int D>
@@ -211,10 +210,46 @@ __device__ inline float band_sq(const u32x4 (&ch)[D / 32], int q) {
   }
 }
 
-template <int D, int P>
+#ifndef TRIA_SCORE_NBI
+#define TRIA_SCORE_NBI 4
+#endif
+
+// 16-key blocks per pipeline stage (d = 256 rows are twice as large: half as many)
+template <int D>
+constexpr int stage_blocks() { return D >= 256 ? (TRIA_SCORE_NBI + 1) / 2 : TRIA_SCORE_NBI; }
+
+// One pipeline stage of a wave: stage_blocks blocks of 16 keys, d/32 16-byte chunks per lane each.
+template <int D>
+using Stage = u32x4[stage_blocks<D>()][D / 32];
+
+// Issues the loads of one stage.  Keys at or past `kend` (the end of the wave's
+// range) are clamped to its last key, whose row is already in cache: their scores
+// are computed but never stored or counted.  Every load is unconditional, so the
+// compiler can keep the next stage in flight while the current one computes.
+template <int D, bool PAGED>
+__device__ inline void load_stage(Stage<D>& ch, const KView& k, int u, int g, int kb, int kend, int col, int grp,
+                                  const int* s_bt, int page0) {
+#pragma unroll
+  for (int b = 0; b < stage_blocks<D>(); ++b) {
+    const int key = min(kb + 16 * b + col, kend - 1);
+    const uint16_t* rp;
+    if (!PAGED) {
+      rp = k.base + (int64_t)u * k.su + (int64_t)g * k.sh + (int64_t)key * k.ss;
+    } else {
+      const int blk = s_bt[key / k.bs - page0];
+      rp = k.base + ((int64_t)blk * k.bs + key % k.bs) * k.ss + (int64_t)g * k.sh;
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) ch[b][i] = *reinterpret_cast<const u32x4*>(rp + chunk_elem<D>(i, grp));
+  }
+}
+
+template <int D, int P, bool PAGED>
 __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   using S = Shape<D>;
+  constexpr int NBI = stage_blocks<D>();
   constexpr int KPW = kScoreTile / 4;  // keys per wave
+  constexpr int STAGE = 16 * NBI;      // keys per pipeline stage
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
@@ -225,7 +260,26 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   const int g = ug % a.hkv;
   const int G = a.group;
   const int hq = a.hkv * G;
-  const int n = clamp_len(a.len, u, a.n_max, a.flags);
+  const int n = clamp_len(a.len, u, a.n_max, threadIdx.x == 0 ? a.flags : nullptr);
+  const int tile0 = tile * kScoreTile;
+
+  // ---- paged caches: the tile's block ids, staged in LDS (checked once)
+  __shared__ int s_bt[PAGED ? kScoreTile + 1 : 1];
+  int page0 = 0;
+  if (PAGED) {
+    page0 = tile0 / a.k.bs;
+    const int last = min(tile0 + kScoreTile, n) - 1;
+    const int npages = last >= tile0 ? last / a.k.bs - page0 + 1 : 0;
+    for (int i = threadIdx.x; i < npages; i += 256) {
+      int blk = a.k.bt[(int64_t)u * a.k.mb + page0 + i];
+      if (blk < 0 || blk >= a.k.npb) {
+        raise_flag(a.flags, kFlagBlock);
+        blk = 0;  // any in-pool block: the scores of this page are unspecified
+      }
+      s_bt[i] = blk;
+    }
+    __syncthreads();
+  }
 
   // ---- B operands of this lane's column
   int head = -1;
@@ -275,24 +329,13 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   double msum = 0.0, msq = 0.0;
   int mcnt = 0;
 
-  const int kw0 = tile * kScoreTile + wave * KPW;
-  for (int it = 0; it < KPW; it += 16 * S::NBI) {
-    const int kb = kw0 + it;
-    if (kb >= n) break;
-    u32x4 ch[S::NBI][S::NKC];
+  const int kw0 = tile0 + wave * KPW;
+  const int kend = min(kw0 + KPW, n);   // this wave's keys: [kw0, kend)
+
+  // scores of one loaded stage: magnitudes, MFMA chain, hi+lo merge, store, moments
+  auto compute = [&](const Stage<D>& ch, int kb) {
 #pragma unroll
-    for (int b = 0; b < S::NBI; ++b) {
-      const int key = kb + 16 * b + col;
-      const uint16_t* rp = key < n ? row_ptr(a.k, u, g, key, a.flags) : nullptr;
-#pragma unroll
-      for (int i = 0; i < S::NKC; ++i) {
-        if (rp) ch[b][i] = *reinterpret_cast<const u32x4*>(rp + chunk_elem<D>(i, grp));
-        else ch[b][i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < S::NBI; ++b) {
-      // magnitudes of the lane's bands, hi/lo bf16
+    for (int b = 0; b < NBI; ++b) {
       bf16x8 mhi[S::NNC], mlo[S::NNC];
 #pragma unroll
       for (int i = 0; i < S::NNC; ++i) {
@@ -327,17 +370,17 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
       }
       if (owner) {
         const int r0 = kb + 16 * b + 4 * grp;
-        if (r0 + 3 < n) {
+        if (r0 + 3 < kend) {
           *reinterpret_cast<f32x4*>(raw_row + r0) = sc;
         } else {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            if (r0 + t < n) raw_row[r0 + t] = sc[t];
+            if (r0 + t < kend) raw_row[r0 + t] = sc[t];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = r0 + t;
-          if (r >= c_lo && r < c_hi) {
+          if (r >= c_lo && r < c_hi && r < kend) {
             const double v = (double)sc[t];
             msum += v;
             msq += v * v;
@@ -345,6 +388,21 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
           }
         }
       }
+    }
+  };
+
+  // ---- two-stage register pipeline over the wave's keys [kw0, kend): the loads of
+  // the next stage are in flight while the current stage computes
+  if (kw0 < kend) {
+    Stage<D> cA, cB;
+    load_stage<D, PAGED>(cA, a.k, u, g, kw0, kend, col, grp, s_bt, page0);
+    for (int kb = kw0;; kb += 2 * STAGE) {
+      load_stage<D, PAGED>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
+      compute(cA, kb);
+      if (kb + STAGE >= kend) break;
+      load_stage<D, PAGED>(cA, a.k, u, g, kb + 2 * STAGE, kend, col, grp, s_bt, page0);
+      compute(cB, kb + STAGE);
+      if (kb + 2 * STAGE >= kend) break;
     }
   }
 
@@ -628,14 +686,24 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s) {
   const long blocks = (long)a.n_units * a.hkv * a.n_tiles;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), blk(256);
-#define TRIA_SCORE_CASE(DD, PP) \
-  if (d == DD && pairing == PP) { hipLaunchKernelGGL((k_score<DD, PP>), grid, blk, 0, s, a); return hipGetLastError(); }
-  TRIA_SCORE_CASE(64, 0)
-  TRIA_SCORE_CASE(64, 1)
-  TRIA_SCORE_CASE(128, 0)
-  TRIA_SCORE_CASE(128, 1)
-  TRIA_SCORE_CASE(256, 0)
-  TRIA_SCORE_CASE(256, 1)
+  const bool paged = a.k.bt != nullptr;
+#define TRIA_SCORE_CASE(DD, PP, PG)                                        \
+  if (d == DD && pairing == PP && paged == PG) {                           \
+    hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, 0, s, a);        \
+    return hipGetLastError();                                              \
+  }
+  TRIA_SCORE_CASE(64, 0, false)
+  TRIA_SCORE_CASE(64, 1, false)
+  TRIA_SCORE_CASE(128, 0, false)
+  TRIA_SCORE_CASE(128, 1, false)
+  TRIA_SCORE_CASE(256, 0, false)
+  TRIA_SCORE_CASE(256, 1, false)
+  TRIA_SCORE_CASE(64, 0, true)
+  TRIA_SCORE_CASE(64, 1, true)
+  TRIA_SCORE_CASE(128, 0, true)
+  TRIA_SCORE_CASE(128, 1, true)
+  TRIA_SCORE_CASE(256, 0, true)
+  TRIA_SCORE_CASE(256, 1, true)
 #undef TRIA_SCORE_CASE
   return hipErrorInvalidValue;
 }
