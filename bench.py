@@ -86,6 +86,30 @@ def cpu_baseline(cfg, seconds: float) -> dict:
             "host_cpus": os.cpu_count()}
 
 
+def copy_probe(gb: float, steps: int) -> int:
+    """A plain copy of a known number of bytes (torch's copy kernel): its time gives the
+    achievable streaming bandwidth, and its FETCH_SIZE / WRITE_SIZE counters the factor
+    that turns counter readings into bytes."""
+    import torch
+    n = int(gb * 1e9) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
+                      "GBps_read_plus_write": 2 * n / (ms / 1e3) / 1e9}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +117,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="qwen3_8b")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
+    ap.add_argument("--input-cache", default="", metavar="DIR",
+                    help="keep the generated K/V caches as .npy files in DIR and reuse them")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GB",
+                    help="instead of the pass, time a plain device-to-device copy of GB gigabytes "
+                         "(the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the pass shards with no "
@@ -100,13 +129,29 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_probe > 0:
+        return copy_probe(args.copy_probe, args.steps)
     from key_importance_scoring_amd import _lib as L
     from key_importance_scoring_amd import synth
     from key_importance_scoring_amd.device import DeviceProblem
 
     cfg = synth.CONFIGS[args.config]
     print(f"[bench] building {cfg.name} inputs", file=sys.stderr, flush=True)
-    prob = DeviceProblem(cfg, device="cuda:0", keep_raw=True)
+    hosts = {}
+    if args.input_cache:
+        import numpy as np
+        from key_importance_scoring_amd.device import host_cache
+        os.makedirs(args.input_cache, exist_ok=True)
+        for which in ("k", "v"):
+            path = os.path.join(args.input_cache, f"{cfg.name}_s{cfg.seed}_{which}.npy")
+            if os.path.exists(path):
+                hosts[which] = np.load(path, mmap_mode="r")
+            else:
+                hosts[which] = host_cache(cfg, which)
+                np.save(path, hosts[which])
+    # the pass as a serving engine runs it: aggregates only, no per-query-head scores
+    prob = DeviceProblem(cfg, device="cuda:0", keep_raw=False, k_host=hosts.get("k"), v_host=hosts.get("v"))
+    hosts.clear()
     stream = torch.cuda.current_stream()
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -78,7 +78,10 @@ enum {
                             len > budget: the top-B rule is still applied     */
   TRIA_FLAG_BLOCK = 8,   /* block id outside [0, n_pool_blocks): row skipped   */
   TRIA_FLAG_INDEX = 16,  /* compaction index outside [0, len[u]): row skipped  */
-  TRIA_FLAG_BMAX = 32    /* min(budget, len) > b_max: clamped to b_max         */
+  TRIA_FLAG_BMAX = 32,   /* min(budget, len) > b_max: clamped to b_max         */
+  TRIA_FLAG_SYNC = 64    /* tria_score: a group of tiles did not all publish
+                            their moments within the bounded wait; the
+                            aggregates of that (unit, KV head) are unspecified */
 };
 
 /* Shape and method parameters (a host struct, read during the call only). */
@@ -116,12 +119,11 @@ typedef struct tria_kv_view {
                                  against it on the device                       */
 } tria_kv_view;
 
-/* Bytes of workspace tria_score and tria_select need for `n_units` units of at
- * most `n_max` slots.  With `raw_in_workspace` != 0 the per-query-head scores
- * are kept in the workspace (tria_score's `raw` may then be NULL).  Returns 0
- * for invalid parameters. */
-size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max,
-                           int32_t raw_in_workspace);
+/* Bytes of workspace tria_score needs for `n_units` units of at most `n_max`
+ * slots (tria_select needs none; given one, it records device flags in it).  The first 256 bytes hold the device flag word: zero them once
+ * before first use (tria_device_flags clears them on every read).  Returns 0 for
+ * invalid parameters. */
+size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max);
 
 /* tria_score - the offset-averaged TriAttention score, z-normalised and
  * aggregated onto each KV head.
@@ -152,10 +154,16 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max,
  *               [device] fp32 [L][G*Hkv][d/2] calibrated query statistics
  *               E[Re q_f], E[Im q_f], E|q_f| [Calib issue]
  *   raw         [device] fp32 [U][G*Hkv][n_max] per-query-head scores, or NULL
- *               (then the workspace must have been sized with raw_in_workspace)
+ *               when they are not wanted (the pass never needs them: the
+ *               aggregation is fused into the score kernel)
  *   agg         [device] fp32 [U][Hkv][n_max] aggregated scores; slots >= len[u]
  *               are left untouched
  *   ws          [device] workspace of ws_bytes >= tria_workspace_size(...)
+ * Execution: the keys of each (unit, KV head) are scored in tiles of 2048 by
+ * concurrent workgroups that exchange their tile moments through the workspace
+ * and wait (boundedly) for one another before normalising; this relies on the
+ * hardware dispatching a kernel's workgroups in order, and reports
+ * TRIA_FLAG_SYNC instead of hanging if a wait ever expires.
  */
 tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
                        const int32_t* len, const int32_t* unit_layer, const int32_t* q_pos,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtria.so"
 TRIA_OK, TRIA_EINVAL, TRIA_ESHAPE, TRIA_EBUDGET, TRIA_EOVERLAP, TRIA_EWORKSPACE, TRIA_ELAUNCH = range(7)
 PAIR_NEOX, PAIR_INTERLEAVED = 0, 1
 AGG_MEAN, AGG_MAX = 0, 1
-FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX = 1, 2, 4, 8, 16, 32
+FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
            "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name")
@@ -54,7 +54,7 @@ def load() -> ctypes.CDLL:
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m key_importance_scoring_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.tria_workspace_size.restype = c_size_t
-    lib.tria_workspace_size.argtypes = [POINTER(TriaParams), c_int32, c_int32, c_int32]
+    lib.tria_workspace_size.argtypes = [POINTER(TriaParams), c_int32, c_int32]
     lib.tria_score.restype = c_int32
     lib.tria_score.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), c_int32, c_int32,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -126,8 +126,8 @@ def _check(status: int) -> None:
 
 # ----------------------------------------------------------------------------- entry points
 
-def tria_workspace_size(p: TriaParams, n_units: int, n_max: int, raw_in_workspace: bool) -> int:
-    return int(load().tria_workspace_size(ctypes.byref(p), n_units, n_max, int(bool(raw_in_workspace))))
+def tria_workspace_size(p: TriaParams, n_units: int, n_max: int) -> int:
+    return int(load().tria_workspace_size(ctypes.byref(p), n_units, n_max))
 
 
 def tria_score(p: TriaParams, k: TriaKvView, n_units: int, n_max: int, len_, unit_layer, q_pos,

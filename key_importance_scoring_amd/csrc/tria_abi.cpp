@@ -27,8 +27,8 @@ tria_status fail(tria_status s, const char* fmt, ...) {
 }
 
 // ------------------------------------------------------------------ timing
-enum { kIdCoef = 0, kIdScore, kIdAgg, kIdSelect, kIdCompact, kNumIds };
-const char* const kNames[kNumIds] = {"k_coef", "k_score", "k_agg", "k_select", "k_compact"};
+enum { kIdCoef = 0, kIdScore, kIdSelect, kIdCompact, kNumIds };
+const char* const kNames[kNumIds] = {"k_coef", "k_score", "k_select", "k_compact"};
 
 struct Rec {
   int id;
@@ -132,16 +132,18 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 
 // ------------------------------------------------------------------ workspace
 struct Layout {
-  size_t C, N, part, raw, total;
+  size_t C, N, part, arrive, total;
   int32_t n_tiles;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Layout layout(const tria_params* p, int32_t n_units, int32_t n_max, bool raw_ws) {
+// Workspace: [flag word | coefficients C | norm weights N | tile moments | arrival counters]
+Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   Layout L{};
   const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
-  L.n_tiles = (n_max + tria::kScoreTile - 1) / tria::kScoreTile;
+  const int tile = tria::score_tile_keys(p->group);
+  L.n_tiles = (n_max + tile - 1) / tile;
   size_t off = 256;  // flag word
   L.C = off;
   off += al256(U * hq * d * 4);
@@ -149,8 +151,8 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max, bool raw_ws)
   off += al256(U * hq * (d / 2) * 4);
   L.part = off;
   off += al256(U * hq * (size_t)L.n_tiles * 3 * 8);
-  L.raw = off;
-  if (raw_ws) off += al256(U * hq * (size_t)n_max * 4);
+  L.arrive = off;
+  off += al256(U * (size_t)p->n_kv_heads * 4 + 4);  // + the tile claim counter
   L.total = off;
   return L;
 }
@@ -159,9 +161,9 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max, bool raw_ws)
 
 extern "C" {
 
-size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max, int32_t raw_in_workspace) {
+size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max) {
   if (check_params(p) != TRIA_OK || n_units < 0 || n_max < 0) return 0;
-  return layout(p, n_units, n_max, raw_in_workspace != 0).total;
+  return layout(p, n_units, n_max).total;
 }
 
 tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
@@ -179,10 +181,16 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
     return fail(TRIA_ESHAPE, "raw and agg must be 16-byte aligned");
   if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(TRIA_EWORKSPACE, "workspace must be 256-byte aligned");
-  const Layout L = layout(p, n_units, n_max, raw == nullptr);
+  const Layout L = layout(p, n_units, n_max);
   if (ws_bytes < L.total)
     return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if (n_units == 0 || n_max == 0) return TRIA_OK;
+  // the tiles of one (unit, KV head) wait for each other: they must all fit at once
+  const int cap = tria::score_capacity(p->head_dim, p->pairing, k->block_table != nullptr, p->group);
+  if (cap < 0) return fail(TRIA_ELAUNCH, "k_score occupancy query failed");
+  if (L.n_tiles > cap)
+    return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the device holds %d",
+                n_max, L.n_tiles, cap);
 
   char* w = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -190,26 +198,24 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   float* C = reinterpret_cast<float*>(w + L.C);
   float* N = reinterpret_cast<float*>(w + L.N);
   double* part = reinterpret_cast<double*>(w + L.part);
-  float* rawp = raw ? raw : reinterpret_cast<float*>(w + L.raw);
+  int32_t* arrive = reinterpret_cast<int32_t*>(w + L.arrive);
+  int32_t* next_tile = arrive + (size_t)n_units * p->n_kv_heads;
 
   tria::Offsets offs{};
   offs.n = p->n_offsets;
   for (int i = 0; i < p->n_offsets; ++i) offs.v[i] = (double)p->offsets[i];
 
-  tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->head_dim, p->n_layers, p->pairing, std::log(p->rope_base),
-                    len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, C, N, flags};
+  tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->n_kv_heads, p->head_dim, p->n_layers, p->pairing,
+                    std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, C, N,
+                    arrive, next_tile, flags};
   hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 
-  tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window, L.n_tiles,
-                     len, C, N, rawp, part, flags};
+  tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
+                     tria::score_tile_keys(p->group), L.n_tiles, p->agg,
+                     len, C, N, raw, part, agg, arrive, next_tile, flags};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, s); });
-  if ((st = launch_status(e, "k_score")) != TRIA_OK) return st;
-
-  tria::AggArgs aa{n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window, L.n_tiles,
-                   (n_max + tria::kAggTile - 1) / tria::kAggTile, p->agg, len, rawp, part, agg};
-  e = timed(kIdAgg, s, [&] { return tria::launch_agg(aa, s); });
-  return launch_status(e, "k_agg");
+  return launch_status(e, "k_score");
 }
 
 tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,

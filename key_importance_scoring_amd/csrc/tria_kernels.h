@@ -9,8 +9,10 @@ namespace tria {
 
 constexpr int kMaxOffsets = 256;
 constexpr int kMaxGroup = 8;
-constexpr int kScoreTile = 2048;   // keys per score workgroup
-constexpr int kAggTile = 1024;     // keys per z-norm/GQA workgroup
+constexpr int kScoreTileMax = 2048;
+// keys per score tile: two tiles of scores ([G][tile + 16] fp32 each) live in LDS
+inline int score_tile_keys(int group) { return group <= 4 ? 2048 : 1024; }
+constexpr int kSpinLimit = 1 << 19;  // bounded wait for a group's tile moments (~0.1 s)
 constexpr int kSelectThreads = 1024;
 
 // A cache view with element strides (bf16 elements).
@@ -36,7 +38,7 @@ struct Offsets {
 };
 
 struct CoefArgs {
-  int32_t n_units, hq, d, layers, pairing;
+  int32_t n_units, hq, hkv, d, layers, pairing;
   double log_base;            // ln(theta)
   const int32_t* len;
   const int32_t* unit_layer;
@@ -46,26 +48,23 @@ struct CoefArgs {
   const float* q_abs;
   float* C;                   // [U][Hq][d]
   float* N;                   // [U][Hq][d/2]
+  int32_t* arrive;            // [U][Hkv] arrival counters of k_score, cleared here
+  int32_t* next_tile;         // tile claim counter of k_score, cleared here
   int32_t* flags;
 };
 
 struct ScoreArgs {
   KView k;
-  int32_t n_units, n_max, hkv, group, sink, window, n_tiles;
+  int32_t n_units, n_max, hkv, group, sink, window, tile, n_tiles, agg_mode;
   const int32_t* len;
   const float* C;
   const float* N;
-  float* raw;                 // [U][Hq][n_max]
-  double* part;               // [U][Hq][n_tiles][3]
+  float* raw;                 // [U][Hq][n_max], may be null
+  double* part;               // [U][Hq][n_tiles][3] tile moments (count, sum, sum of squares)
+  float* agg;                 // [U][Hkv][n_max]
+  int32_t* arrive;            // [U][Hkv] tiles that have published their moments
+  int32_t* next_tile;         // next tile to claim
   int32_t* flags;
-};
-
-struct AggArgs {
-  int32_t n_units, n_max, hkv, group, sink, window, n_tiles, n_atiles, agg;
-  const int32_t* len;
-  const float* raw;
-  const double* part;
-  float* out;                 // [U][Hkv][n_max]
 };
 
 struct SelectArgs {
@@ -95,7 +94,9 @@ constexpr int kCompactRows = 64;   // kept rows per compaction workgroup
 
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s);
-hipError_t launch_agg(const AggArgs& a, hipStream_t s);
+// Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
+// of one (unit, KV head) must be resident together for the moment exchange.
+int score_capacity(int d, int pairing, bool paged, int group);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 

@@ -17,9 +17,10 @@
 //               norm weights n_{h,f} = E|q_f| - |E[q_f]|;
 //   k_score   : streams the bf16 K cache once; per key and query head
 //                 s = sum_j C[j] K[j] + sum_f n_f |k_f|
-//               on MFMA (hi/lo bf16 split of the fp32 coefficients), plus fp64
-//               moment partials over the candidate slots;
-//   k_agg     : z-normalisation per query head and GQA mean/max aggregation;
+//               on MFMA (hi/lo bf16 split of the fp32 coefficients).  A tile's
+//               scores stay in LDS; the tiles of one (unit, KV head) exchange their
+//               moments, then each z-normalises its scores per query head,
+//               aggregates the GQA group (mean or max) and writes the aggregate;
 //               protected slots (sinks + recent window) get +inf;
 //   k_select  : top-B per (unit, KV head) by LDS radix select on order-preserving
 //               uint32 keys, ties to the lower slot, kept slots ascending;
@@ -43,7 +44,7 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int32_t kFlagLen = 1, kFlagLayer = 2, kFlagBudget = 4, kFlagBlock = 8, kFlagIndex = 16,
-                  kFlagBmax = 32;
+                  kFlagBmax = 32, kFlagSync = 64;
 
 __device__ inline void raise_flag(int32_t* flags, int32_t bit) {
   if (flags) atomicOr(flags, bit);
@@ -86,9 +87,11 @@ __device__ inline const uint16_t* row_ptr(const V& v, int u, int g, int slot, in
 }
 
 // ============================================================================ k_coef
-// One workgroup per unit.  Per-(band, offset) twiddles e^{i w_f delta} are summed
-// by F x (256/F) threads into LDS partials; W_f and the rotation to q_pos are
-// formed once per band; then every (query head, band) coefficient of the unit.
+// Grid (unit, chunk of 256 (query head, band) pairs).  Per-(band, offset) twiddles
+// e^{i w_f delta} are summed by F x (256/F) threads into LDS partials; W_f and the
+// rotation to q_pos are formed once per band; then each thread forms one (query
+// head, band) coefficient, so the statistics loads of a block are all in flight
+// together.  Block (u, 0) also clears the unit's arrival counters of k_score.
 __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   const int u = blockIdx.x;
   const int F = a.d / 2;
@@ -98,6 +101,23 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   const int s = t / F;
   __shared__ double tw_re[256], tw_im[256];
   __shared__ double rot_re[128], rot_im[128];
+
+  if (blockIdx.y == 0 && t < a.hkv) a.arrive[(size_t)u * a.hkv + t] = 0;
+  if (u == 0 && blockIdx.y == 0 && t == 0) *a.next_tile = 0;
+
+  // statistics of this thread's (query head, band), loaded while the twiddles are formed
+  const int p = blockIdx.y * 256 + t;
+  const int h = p / F, b = p % F;
+  const int layer = a.unit_layer[u];
+  const bool ok = layer >= 0 && layer < a.layers;
+  if (!ok && t == 0 && blockIdx.y == 0) raise_flag(a.flags, kFlagLayer);
+  double mr = 0.0, mi = 0.0, ab = 0.0;
+  if (ok && p < a.hq * F) {
+    const size_t si = ((size_t)layer * a.hq + h) * F + b;
+    mr = a.q_re[si];
+    mi = a.q_im[si];
+    ab = a.q_abs[si];
+  }
 
   // band frequency w_f = theta^(-2f/d)  [Fold note, sec. 2, Eq. 2 bullets]
   const double w = exp(-(2.0 * f / a.d) * a.log_base);
@@ -125,32 +145,20 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     rot_im[t] = wr * sv + wi * cv;
   }
   __syncthreads();
+  if (p >= a.hq * F) return;
 
-  const int layer = a.unit_layer[u];
-  const bool ok = layer >= 0 && layer < a.layers;
-  if (!ok && t == 0) raise_flag(a.flags, kFlagLayer);
-  for (int p = t; p < a.hq * F; p += 256) {
-    const int h = p / F, b = p % F;
-    double mr = 0.0, mi = 0.0, ab = 0.0;
-    if (ok) {
-      const size_t si = ((size_t)layer * a.hq + h) * F + b;
-      mr = a.q_re[si];
-      mi = a.q_im[si];
-      ab = a.q_abs[si];
-    }
-    // c = mu' e^{i w q_pos} with mu' = E[q_f] W_f  [Fold note, Eq. 7]
-    const double cr = mr * rot_re[b] - mi * rot_im[b];
-    const double ci = mr * rot_im[b] + mi * rot_re[b];
-    // Re(c conj(k)) = Re(c) Re(k) + Im(c) Im(k): coefficients sit where the key's
-    // real / imaginary parts sit in the pairing layout  [Calib issue, pairing]
-    float* crow = a.C + ((size_t)u * a.hq + h) * a.d;
-    const int ire = a.pairing == 0 ? b : 2 * b;
-    const int iim = a.pairing == 0 ? b + F : 2 * b + 1;
-    crow[ire] = (float)cr;
-    crow[iim] = (float)ci;
-    // norm weight E|q_f| - |E q_f| = E|q_f| (1 - R_f)  [Blog, The Method; reading]
-    a.N[((size_t)u * a.hq + h) * F + b] = (float)(ab - sqrt(mr * mr + mi * mi));
-  }
+  // c = mu' e^{i w q_pos} with mu' = E[q_f] W_f  [Fold note, Eq. 7]
+  const double cr = mr * rot_re[b] - mi * rot_im[b];
+  const double ci = mr * rot_im[b] + mi * rot_re[b];
+  // Re(c conj(k)) = Re(c) Re(k) + Im(c) Im(k): coefficients sit where the key's
+  // real / imaginary parts sit in the pairing layout  [Calib issue, pairing]
+  float* crow = a.C + ((size_t)u * a.hq + h) * a.d;
+  const int ire = a.pairing == 0 ? b : 2 * b;
+  const int iim = a.pairing == 0 ? b + F : 2 * b + 1;
+  crow[ire] = (float)cr;
+  crow[iim] = (float)ci;
+  // norm weight E|q_f| - |E q_f| = E|q_f| (1 - R_f)  [Blog, The Method; reading]
+  a.N[((size_t)u * a.hq + h) * F + b] = (float)(ab - sqrt(mr * mr + mi * mi));
 }
 
 // ============================================================================ k_score
@@ -191,6 +199,14 @@ __device__ inline int lane_band(int q, int c) {
   return D / 4 + c * (D / 16) + (q - D / 16);         // interleaved, second half
 }
 
+// re^2 + im^2 of a packed bf16 pair (re in the low half), products exact in fp32.
+// Kept as the builtin (not hand-written asm) so the compiler sees the instruction
+// and inserts the wait states its consumers (v_sqrt) need.
+__device__ inline float sq_bf16x2(uint32_t w) {
+  const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
+}
+
 // |k_f|^2 for the lane's band q from its loaded chunks.
 template <int D, int P>
 __device__ inline float band_sq(const u32x4 (&ch)[D / 32], int q) {
@@ -200,13 +216,10 @@ __device__ inline float band_sq(const u32x4 (&ch)[D / 32], int q) {
     const uint32_t re = ch[i][w], im = ch[HC + i][w];
     const uint32_t pr = (q & 1) ? __builtin_amdgcn_perm(im, re, 0x07060302u)
                                 : __builtin_amdgcn_perm(im, re, 0x05040100u);
-    const bf16x2 v = __builtin_bit_cast(bf16x2, pr);
-    return __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
+    return sq_bf16x2(pr);
   } else {
     const int i = q < D / 16 ? q / 4 : HC + (q - D / 16) / 4;
-    const uint32_t wv = ch[i][q % 4];
-    const bf16x2 v = __builtin_bit_cast(bf16x2, wv);
-    return __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
+    return sq_bf16x2(ch[i][q % 4]);
   }
 }
 
@@ -244,31 +257,45 @@ __device__ inline void load_stage(Stage<D>& ch, const KView& k, int u, int g, in
   }
 }
 
+// Per-tile indices.  Tiles of one (unit, KV head) are consecutive: t = ug * n_tiles + tile.
+struct TileInfo {
+  int ug, u, g, tile, n, tile0, tlen;
+};
+
+__device__ inline TileInfo tile_info(const ScoreArgs& a, int t, bool flag) {
+  TileInfo ti;
+  ti.tile = t % a.n_tiles;
+  ti.ug = t / a.n_tiles;
+  ti.u = ti.ug / a.hkv;
+  ti.g = ti.ug % a.hkv;
+  ti.n = clamp_len(a.len, ti.u, a.n_max, flag && threadIdx.x == 0 ? a.flags : nullptr);
+  ti.tile0 = ti.tile * a.tile;
+  ti.tlen = max(0, min(a.tile, ti.n - ti.tile0));
+  return ti;
+}
+
+// Scores one tile into LDS (s_raw, [G][tile + 16]), writes the per-query-head
+// scores if wanted, and publishes the tile's candidate moments.
 template <int D, int P, bool PAGED>
-__global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
+__device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float* s_raw, int* s_bt) {
   using S = Shape<D>;
   constexpr int NBI = stage_blocks<D>();
-  constexpr int KPW = kScoreTile / 4;  // keys per wave
-  constexpr int STAGE = 16 * NBI;      // keys per pipeline stage
+  constexpr int STAGE = 16 * NBI;  // keys per pipeline stage
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int tile = blockIdx.x % a.n_tiles;
-  const int ug = blockIdx.x / a.n_tiles;
-  const int u = ug / a.hkv;
-  const int g = ug % a.hkv;
   const int G = a.group;
   const int hq = a.hkv * G;
-  const int n = clamp_len(a.len, u, a.n_max, threadIdx.x == 0 ? a.flags : nullptr);
-  const int tile0 = tile * kScoreTile;
+  const int RS = a.tile + 16;      // LDS row stride: heads start 16 banks apart
+  const int kpw = a.tile / 4;      // keys per wave
+  const int u = ti.u, g = ti.g, n = ti.n, tile0 = ti.tile0;
 
-  // ---- paged caches: the tile's block ids, staged in LDS (checked once)
-  __shared__ int s_bt[PAGED ? kScoreTile + 1 : 1];
+  // ---- paged caches: the tile's block ids, checked once, in LDS
   int page0 = 0;
   if (PAGED) {
     page0 = tile0 / a.k.bs;
-    const int last = min(tile0 + kScoreTile, n) - 1;
+    const int last = min(tile0 + a.tile, n) - 1;
     const int npages = last >= tile0 ? last / a.k.bs - page0 + 1 : 0;
     for (int i = threadIdx.x; i < npages; i += 256) {
       int blk = a.k.bt[(int64_t)u * a.k.mb + page0 + i];
@@ -324,19 +351,24 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   }
 
   const bool owner = col >= 8 && col < 8 + G;  // lanes that hold a final score
-  const int c_lo = a.sink, c_hi = n - a.window;  // candidates: [sink, n - window)
-  float* raw_row = a.raw + ((size_t)u * hq + g * G + (owner ? col - 8 : 0)) * a.n_max;
-  double msum = 0.0, msq = 0.0;
-  int mcnt = 0;
+  float* s_row = s_raw + (owner ? col - 8 : 0) * RS - tile0;
+  const int kw0 = tile0 + wave * kpw;
+  const int kend = min(kw0 + kpw, n);   // this wave's keys: [kw0, kend)
 
-  const int kw0 = tile0 + wave * KPW;
-  const int kend = min(kw0 + KPW, n);   // this wave's keys: [kw0, kend)
-
-  // scores of one loaded stage: magnitudes, MFMA chain, hi+lo merge, store, moments
+  // scores of one loaded stage: dot-product MFMAs of every block first (independent
+  // accumulators), then per block the magnitudes and the norm-term MFMAs
   auto compute = [&](const Stage<D>& ch, int kb) {
+    f32x4 acc[NBI];
+#pragma unroll
+    for (int b = 0; b < NBI; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < S::NKC; ++i)
+#pragma unroll
+      for (int b = 0; b < NBI; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[b][i]), bdot[i], acc[b], 0,
+                                                         0, 0);
 #pragma unroll
     for (int b = 0; b < NBI; ++b) {
-      bf16x8 mhi[S::NNC], mlo[S::NNC];
 #pragma unroll
       for (int i = 0; i < S::NNC; ++i) {
         u32x4 h4, l4;
@@ -349,45 +381,20 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
           h4[j] = hi;
           l4[j] = lw;
         }
-        mhi[i] = __builtin_bit_cast(bf16x8, h4);
-        mlo[i] = __builtin_bit_cast(bf16x8, l4);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h4), bna[i], acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l4), bnb[i], acc[b], 0, 0, 0);
       }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int i = 0; i < S::NKC; ++i)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[b][i]), bdot[i], acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < S::NNC; ++i) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mhi[i], bna[i], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mlo[i], bnb[i], acc, 0, 0, 0);
-      }
+    for (int b = 0; b < NBI; ++b) {
       // column c + 8 <- column c + column c + 8 (hi + lo of one query head)
       f32x4 sc;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[t]), 0x118, 0xF, 0xF, true);
-        sc[t] = acc[t] + __int_as_float(other);
+        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[b][t]), 0x118, 0xF, 0xF, true);
+        sc[t] = acc[b][t] + __int_as_float(other);
       }
-      if (owner) {
-        const int r0 = kb + 16 * b + 4 * grp;
-        if (r0 + 3 < kend) {
-          *reinterpret_cast<f32x4*>(raw_row + r0) = sc;
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (r0 + t < kend) raw_row[r0 + t] = sc[t];
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = r0 + t;
-          if (r >= c_lo && r < c_hi && r < kend) {
-            const double v = (double)sc[t];
-            msum += v;
-            msq += v * v;
-            mcnt += 1;
-          }
-        }
-      }
+      if (owner) *reinterpret_cast<f32x4*>(s_row + kb + 16 * b + 4 * grp) = sc;
     }
   };
 
@@ -405,100 +412,180 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
       if (kb + 2 * STAGE >= kend) break;
     }
   }
+  __syncthreads();
 
-  // ---- moment partials of the tile: reduce over lane groups, then waves
-  msum += __shfl_xor(msum, 16);
-  msq += __shfl_xor(msq, 16);
-  mcnt += __shfl_xor(mcnt, 16);
-  msum += __shfl_xor(msum, 32);
-  msq += __shfl_xor(msq, 32);
-  mcnt += __shfl_xor(mcnt, 32);
-  __shared__ double red_s[4][8], red_q[4][8];
-  __shared__ int red_c[4][8];
-  if (grp == 0 && owner) {
-    red_s[wave][col - 8] = msum;
-    red_q[wave][col - 8] = msq;
-    red_c[wave][col - 8] = mcnt;
+  // ---- per-query-head scores, if the caller wants them: full lines per head
+  const int tlen = ti.tlen;
+  if (a.raw) {
+    for (int h = 0; h < G; ++h) {
+      float* dst = a.raw + ((size_t)u * hq + g * G + h) * a.n_max + tile0;
+      const float* src = s_raw + h * RS;
+      for (int i = 4 * threadIdx.x; i < tlen; i += 4 * 256) {
+        if (i + 3 < tlen) {
+          *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(src + i);
+        } else {
+          for (int t = i; t < tlen; ++t) dst[t] = src[t];
+        }
+      }
+    }
+  }
+
+  // ---- moments of the tile over its candidate slots [sink, n - window): two
+  // passes over LDS (mean, then squared deviations), one wave per query head.
+  // Published with agent-scope stores: the other tiles of this (unit, KV head)
+  // run on other CUs and XCDs.
+  const int c0 = max(a.sink, tile0) - tile0;
+  const int c1 = min(n - a.window, tile0 + tlen) - tile0;
+  for (int h = wave; h < G; h += 4) {
+    const float* src = s_raw + h * RS;
+    float acc = 0.0f;
+    for (int i = c0 + lane; i < c1; i += 64) acc += src[i];
+    double sum = (double)acc;
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    const int cnt = max(0, c1 - c0);
+    const double mean = cnt > 0 ? sum / cnt : 0.0;
+    const float mf = (float)mean;
+    float q = 0.0f;
+    for (int i = c0 + lane; i < c1; i += 64) {
+      const float dv = src[i] - mf;
+      q = __builtin_fmaf(dv, dv, q);
+    }
+    double m2 = (double)q;
+    for (int o = 32; o > 0; o >>= 1) m2 += __shfl_xor(m2, o);
+    // pass-two deviations are about mf (the mean rounded to fp32): shift back
+    const double dm = mean - (double)mf;
+    m2 -= (double)cnt * dm * dm;
+    if (lane == 0) {
+      unsigned long long* p =
+          reinterpret_cast<unsigned long long*>(a.part + (((size_t)u * hq + g * G + h) * a.n_tiles + ti.tile) * 3);
+      __hip_atomic_store(p + 0, (unsigned long long)__double_as_longlong((double)cnt), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p + 1, (unsigned long long)__double_as_longlong(sum), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p + 2, (unsigned long long)__double_as_longlong(m2 + (double)cnt * mean * mean),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // every publishing store is complete before the arrival below is counted: the
+  // stores and the counter are agent-scope atomics, coherent across XCDs by
+  // themselves, so only their order needs enforcing (an agent-scope release fence
+  // would also write back this XCD's whole L2, once per tile)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.arrive + ti.ug, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every tile of the (unit, KV head) of `ti` has published its moments,
+// then z-normalises the tile's scores (still in LDS) per query head, aggregates the
+// GQA group onto the KV head [Fold note, sec. 4: normalize-then-max; mean is the
+// other variant] and writes the aggregate; protected slots (sinks, recent window)
+// get +inf.
+__device__ inline void finalize_tile(const ScoreArgs& a, const TileInfo& ti, const float* s_raw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = a.group;
+  const int hq = a.hkv * G;
+  const int RS = a.tile + 16;
+  __shared__ float s_mean[kMaxGroup], s_inv[kMaxGroup];
+  if (threadIdx.x == 0) {
+    const int32_t* ctr = a.arrive + ti.ug;
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_tiles) {
+      __builtin_amdgcn_s_sleep(8);
+      if (++spins >= kSpinLimit) {
+        raise_flag(a.flags, kFlagSync);
+        break;
+      }
+    }
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    double s = 0.0, q = 0.0;
-    int c = 0;
-    for (int w = 0; w < 4; ++w) {
-      s += red_s[w][h];
-      q += red_q[w][h];
-      c += red_c[w][h];
+
+  // the group's mean and standard deviation per query head (fixed summation order:
+  // lane j takes tiles j, j + 64, ...; then a fixed shuffle tree)
+  for (int h = wave; h < G; h += 4) {
+    const unsigned long long* p =
+        reinterpret_cast<const unsigned long long*>(a.part + ((size_t)ti.u * hq + ti.g * G + h) * a.n_tiles * 3);
+    double c = 0.0, s1 = 0.0, s2 = 0.0;
+    for (int j = lane; j < a.n_tiles; j += 64) {
+      c += __longlong_as_double(__hip_atomic_load(p + 3 * j + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      s1 += __longlong_as_double(__hip_atomic_load(p + 3 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      s2 += __longlong_as_double(__hip_atomic_load(p + 3 * j + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
-    double* p = a.part + (((size_t)u * hq + g * G + h) * a.n_tiles + tile) * 3;
-    p[0] = (double)c;
-    p[1] = s;
-    p[2] = q;
+    for (int o = 32; o > 0; o >>= 1) {
+      c += __shfl_xor(c, o);
+      s1 += __shfl_xor(s1, o);
+      s2 += __shfl_xor(s2, o);
+    }
+    if (lane == 0) {
+      const double m = c > 0.0 ? s1 / c : 0.0;
+      const double var = c > 0.0 ? fmax(s2 / c - m * m, 0.0) : 0.0;
+      s_mean[h] = (float)m;
+      s_inv[h] = (float)(1.0 / fmax(sqrt(var), 1e-12));
+    }
+  }
+  __syncthreads();
+
+  const int tlen = ti.tlen, tile0 = ti.tile0, n = ti.n;
+  float* dst = a.agg + ((size_t)ti.u * a.hkv + ti.g) * a.n_max + tile0;
+  const float invg = 1.0f / (float)G;
+  for (int i = 4 * threadIdx.x; i < tlen; i += 4 * 256) {
+    f32x4 out;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) out[t] = a.agg_mode == 0 ? 0.0f : -__builtin_inff();
+    for (int h = 0; h < G; ++h) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(s_raw + h * RS + i);
+      const float m = s_mean[h], inv = s_inv[h];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float z = (v[t] - m) * inv;
+        out[t] = a.agg_mode == 0 ? out[t] + z : fmaxf(out[t], z);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = tile0 + i + t;
+      if (a.agg_mode == 0) out[t] *= invg;
+      if (key < a.sink || key >= n - a.window) out[t] = __builtin_inff();
+    }
+    if (i + 3 < tlen) {
+      *reinterpret_cast<f32x4*>(dst + i) = out;
+    } else {
+      for (int t = 0; t < 4 && i + t < tlen; ++t) dst[i + t] = out[t];
+    }
   }
 }
 
-// ============================================================================ k_agg
-// z-normalisation per query head over the candidate slots, then GQA aggregation.
-__global__ __launch_bounds__(256) void k_agg(AggArgs a) {
-  const int at = blockIdx.x % a.n_atiles;
-  const int ug = blockIdx.x / a.n_atiles;
-  const int u = ug / a.hkv;
-  const int g = ug % a.hkv;
+// Persistent score kernel: as many workgroups as fit on the device claim tiles in
+// order from a counter.  Each workgroup scores and publishes its current tile, and
+// only then finalises its previous one (two LDS score buffers): by that time the
+// previous tile's group has nearly always published, so the moment exchange hides
+// behind the streaming.  A workgroup waits only on tiles that are already
+// claimed-and-published or claimed by running workgroups that publish before they
+// wait; with P workgroups each holding at most two tiles, a circular wait would
+// need 2P <= n_tiles, and P >= n_tiles (the host checks it), so the wait always ends
+// (it is also bounded, and flagged, as a last resort).
+template <int D, int P, bool PAGED>
+__global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
+  extern __shared__ float s_dyn[];
+  __shared__ int s_t;
   const int G = a.group;
-  const int hq = a.hkv * G;
-  int n = a.len[u];
-  n = n < 0 ? 0 : (n > a.n_max ? a.n_max : n);
-  __shared__ float mean_s[kMaxGroup], inv_s[kMaxGroup];
-  if ((int)threadIdx.x < G) {
-    const double* p = a.part + ((size_t)u * hq + g * G + threadIdx.x) * a.n_tiles * 3;
-    double c = 0.0, s = 0.0, q = 0.0;
-    for (int i = 0; i < a.n_tiles; ++i) {
-      c += p[3 * i];
-      s += p[3 * i + 1];
-      q += p[3 * i + 2];
-    }
-    const double m = c > 0.0 ? s / c : 0.0;
-    const double var = c > 0.0 ? fmax(q / c - m * m, 0.0) : 0.0;
-    mean_s[threadIdx.x] = (float)m;
-    inv_s[threadIdx.x] = (float)(1.0 / fmax(sqrt(var), 1e-12));
-  }
-  __syncthreads();
-  const int k0 = at * kAggTile + 4 * threadIdx.x;
-  if (k0 >= n) return;
-  f32x4 out;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) out[t] = a.agg == 0 ? 0.0f : -__builtin_inff();
-  const bool full = k0 + 3 < n;
-  for (int h = 0; h < G; ++h) {
-    const float* row = a.raw + ((size_t)u * hq + g * G + h) * a.n_max;
-    f32x4 v;
-    if (full) {
-      v = *reinterpret_cast<const f32x4*>(row + k0);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = k0 + t < n ? row[k0 + t] : 0.0f;
-    }
-    const float m = mean_s[h], inv = inv_s[h];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float z = (v[t] - m) * inv;
-      out[t] = a.agg == 0 ? out[t] + z : fmaxf(out[t], z);
-    }
-  }
-  const float invg = 1.0f / (float)G;
-  float* dst = a.out + ((size_t)u * a.hkv + g) * a.n_max;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int k = k0 + t;
-    if (a.agg == 0) out[t] *= invg;
-    if (k < a.sink || k >= n - a.window) out[t] = __builtin_inff();
-  }
-  if (full) {
-    *reinterpret_cast<f32x4*>(dst + k0) = out;
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (k0 + t < n) dst[k0 + t] = out[t];
+  const int RS = a.tile + 16;
+  float* buf0 = s_dyn;
+  float* buf1 = s_dyn + G * RS;
+  int* s_bt = reinterpret_cast<int*>(s_dyn + 2 * G * RS);
+  const int total = a.n_units * a.hkv * a.n_tiles;
+  int prev = -1;
+  bool b = false;
+  for (;;) {
+    if (threadIdx.x == 0) s_t = atomicAdd(a.next_tile, 1);
+    __syncthreads();
+    const int t = s_t;
+    __syncthreads();
+    if (t < total) score_phase<D, P, PAGED>(a, tile_info(a, t, true), b ? buf1 : buf0, s_bt);
+    if (prev >= 0) finalize_tile(a, tile_info(a, prev, false), b ? buf0 : buf1);
+    if (t >= total) break;
+    prev = t;
+    b = !b;
   }
 }
 
@@ -678,18 +765,53 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 // ============================================================================ launches
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   if (a.n_units == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_coef, dim3(a.n_units), dim3(256), 0, s, a, offs);
+  const unsigned chunks = (unsigned)((a.hq * (a.d / 2) + 255) / 256);
+  hipLaunchKernelGGL(k_coef, dim3(a.n_units, chunks), dim3(256), 0, s, a, offs);
   return hipGetLastError();
 }
 
+size_t score_lds(int group, bool paged) {
+  const int tile = score_tile_keys(group);
+  return (size_t)2 * group * (tile + 16) * 4 + (paged ? (size_t)(tile + 1) * 4 : 0);
+}
+
+int score_capacity(int d, int pairing, bool paged, int group) {
+  const size_t lds = score_lds(group, paged);
+  int per_cu = 0, dev = 0, cus = 0;
+  hipError_t e = hipErrorInvalidValue;
+#define TRIA_OCC_CASE(DD, PP, PG)                                                                       \
+  if (d == DD && pairing == PP && paged == PG)                                                          \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_score<DD, PP, PG>, 256, lds);
+  TRIA_OCC_CASE(64, 0, false)
+  TRIA_OCC_CASE(64, 1, false)
+  TRIA_OCC_CASE(128, 0, false)
+  TRIA_OCC_CASE(128, 1, false)
+  TRIA_OCC_CASE(256, 0, false)
+  TRIA_OCC_CASE(256, 1, false)
+  TRIA_OCC_CASE(64, 0, true)
+  TRIA_OCC_CASE(64, 1, true)
+  TRIA_OCC_CASE(128, 0, true)
+  TRIA_OCC_CASE(128, 1, true)
+  TRIA_OCC_CASE(256, 0, true)
+  TRIA_OCC_CASE(256, 1, true)
+#undef TRIA_OCC_CASE
+  if (e != hipSuccess) return -1;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return per_cu * cus;
+}
+
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s) {
-  const long blocks = (long)a.n_units * a.hkv * a.n_tiles;
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), blk(256);
+  const long tiles = (long)a.n_units * a.hkv * a.n_tiles;
+  if (tiles == 0) return hipSuccess;
   const bool paged = a.k.bt != nullptr;
+  const int cap = score_capacity(d, pairing, paged, a.group);
+  if (cap < a.n_tiles) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
+  const size_t lds = score_lds(a.group, paged);
 #define TRIA_SCORE_CASE(DD, PP, PG)                                        \
   if (d == DD && pairing == PP && paged == PG) {                           \
-    hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, 0, s, a);        \
+    hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, lds, s, a);      \
     return hipGetLastError();                                              \
   }
   TRIA_SCORE_CASE(64, 0, false)
@@ -706,13 +828,6 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s) {
   TRIA_SCORE_CASE(256, 1, true)
 #undef TRIA_SCORE_CASE
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_agg(const AggArgs& a, hipStream_t s) {
-  const long blocks = (long)a.n_units * a.hkv * a.n_atiles;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_agg, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {

@@ -31,6 +31,19 @@ def params_for(cfg: synth.Config) -> L.TriaParams:
                          cfg.rope_base, cfg.offsets, cfg.sink, cfg.window)
 
 
+def host_cache(cfg: synth.Config, which: str, workers: int | None = None) -> np.ndarray:
+    """The K (``"k"``) or V (``"v"``) cache of a workload as bf16 bits, in the layout the
+    device holds it: a paged pool, or dense [U][Hkv][n_max][d] padded to n_max slots
+    (n_max = the longest unit rounded up to 16)."""
+    if cfg.paged:
+        return synth.build_cache(cfg, which, workers)
+    n_max = round_up(max(synth.units(cfg).n_max, 1), 16)
+    out = np.zeros((cfg.n_units, cfg.n_kv_heads, n_max, cfg.head_dim), dtype=np.uint16)
+    for unit, head, rows in synth.iter_chunks(cfg, which, workers):
+        out[unit, head, :rows.shape[0]] = rows
+    return out
+
+
 class DeviceProblem:
     """One workload resident in HBM, plus its outputs and workspace."""
 
@@ -79,7 +92,7 @@ class DeviceProblem:
             self.vd_view = L.make_view(self.V_out, Hkv * self.b_max * d, self.b_max * d, d)
 
         # --- per-unit metadata and statistics
-        to = lambda a, dt=torch.int32: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev, dt)
+        to = lambda a, dt=torch.int32: torch.from_numpy(np.array(a, copy=True)).to(self.dev, dt)
         self.len = to(u.lengths)
         self.unit_layer = to(u.unit_layer)
         self.q_pos = to(u.q_pos)
@@ -98,20 +111,11 @@ class DeviceProblem:
         self.idx = torch.zeros((U, Hkv, self.b_max), dtype=torch.int32, device=self.dev)
         self.cnt = torch.zeros((U,), dtype=torch.int32, device=self.dev)
         self.pos_out = torch.zeros((U, Hkv, self.b_max), dtype=torch.int32, device=self.dev)
-        self.ws_bytes = L.tria_workspace_size(self.params, U, self.n_max, self.raw is None)
+        self.ws_bytes = L.tria_workspace_size(self.params, U, self.n_max)
         self.ws = torch.zeros((self.ws_bytes,), dtype=torch.uint8, device=self.dev)
 
     def _host_cache(self, which: str, workers) -> np.ndarray:
-        cfg = self.cfg
-        if cfg.paged:
-            return synth.build_cache(cfg, which, workers)
-        # dense caches padded to n_max slots
-        u = self.units
-        out = np.zeros((cfg.n_units, cfg.n_kv_heads, self.n_max, cfg.head_dim), dtype=np.uint16)
-        for unit, head, rows in synth.iter_chunks(cfg, which, workers):
-            out[unit, head, :rows.shape[0]] = rows
-        del u
-        return out
+        return host_cache(self.cfg, which, workers)
 
     # ------------------------------------------------------------------ the pass
     def score(self, stream=None):

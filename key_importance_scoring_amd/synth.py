@@ -315,11 +315,17 @@ def iter_chunks(cfg: Config, which: str, workers: int | None = None):
     """Yield (unit, kv_head, rows) for every chunk of the K (``"k"``) or V (``"v"``) cache.
 
     With ``workers > 1`` the chunks are drawn in a spawned process pool (no GPU state
-    is inherited); the order of the yielded chunks is then arbitrary.
+    is inherited); the order of the yielded chunks is then arbitrary.  The default
+    pool size can be set with the environment variable TRIA_SYNTH_WORKERS (1 keeps
+    everything in-process, e.g. under a profiler that attaches to every process).
     """
     jobs = _jobs(cfg, which)
     if workers is None:
-        workers = min(16, os.cpu_count() or 1) if len(jobs) > 16 else 1
+        env = os.environ.get("TRIA_SYNTH_WORKERS")
+        if env:
+            workers = int(env)
+        else:
+            workers = min(16, os.cpu_count() or 1) if len(jobs) > 16 else 1
     if workers <= 1:
         for j in jobs:
             yield _chunk_job(j)

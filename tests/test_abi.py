@@ -45,7 +45,7 @@ def _score(p=None, k=None, n_units=2, n_max=4096, ws_bytes=None, raw=None, **kw)
     p = p or _params()
     k = k or _view()
     if ws_bytes is None:
-        ws_bytes = L.tria_workspace_size(p, n_units, n_max, raw is None)
+        ws_bytes = L.tria_workspace_size(p, n_units, n_max)
     args = dict(len_=A, unit_layer=A, q_pos=A, q_mean_re=A, q_mean_im=A, q_abs_mean=A, raw=raw, agg=A, ws=WS)
     args.update(kw)
     L.tria_score(p, k, n_units, n_max, args["len_"], args["unit_layer"], args["q_pos"], args["q_mean_re"],
@@ -72,19 +72,20 @@ def test_strerror_and_kernel_names():
     for s in range(7):
         assert lib.tria_strerror(s)
     assert lib.tria_strerror(99) == b"unknown status"
-    names = [lib.tria_kernel_name(i) for i in range(5)]
-    assert names == [b"k_coef", b"k_score", b"k_agg", b"k_select", b"k_compact"]
-    assert lib.tria_kernel_name(5) == b""
+    names = [lib.tria_kernel_name(i) for i in range(4)]
+    assert names == [b"k_coef", b"k_score", b"k_select", b"k_compact"]
+    assert lib.tria_kernel_name(4) == b""
 
 
 def test_workspace_size_grows_with_the_problem():
     p = _params()
-    a = L.tria_workspace_size(p, 2, 4096, False)
-    b = L.tria_workspace_size(p, 2, 4096, True)
-    assert a > 0 and b - a >= 2 * 32 * 4096 * 4
-    assert L.tria_workspace_size(p, 4, 4096, False) > a
-    assert L.tria_workspace_size(_params(head_dim=96), 2, 4096, False) == 0
-    assert L.tria_workspace_size(p, -1, 4096, False) == 0
+    a = L.tria_workspace_size(p, 2, 4096)
+    # flag word + coefficients [U][Hq][d] + norm weights [U][Hq][d/2] + tile moments + counters
+    assert a >= 256 + 2 * 32 * 128 * 4 + 2 * 32 * 64 * 4 + 2 * 32 * 2 * 3 * 8 + 2 * 8 * 4
+    assert L.tria_workspace_size(p, 4, 4096) > a
+    assert L.tria_workspace_size(p, 2, 8192) > a
+    assert L.tria_workspace_size(_params(head_dim=96), 2, 4096) == 0
+    assert L.tria_workspace_size(p, -1, 4096) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -129,11 +130,8 @@ def test_score_shape_and_workspace_checks():
     assert _status(lambda: _score(agg=A + 4)) == L.TRIA_ESHAPE
     assert _status(lambda: _score(ws=None)) == L.TRIA_EWORKSPACE
     assert _status(lambda: _score(ws=WS + 64)) == L.TRIA_EWORKSPACE      # 256-byte alignment
-    need = L.tria_workspace_size(_params(), 2, 4096, True)
+    need = L.tria_workspace_size(_params(), 2, 4096)
     assert _status(lambda: _score(ws_bytes=need - 1)) == L.TRIA_EWORKSPACE
-    # without raw the workspace must also hold the per-query-head scores
-    small = L.tria_workspace_size(_params(), 2, 4096, False)
-    assert _status(lambda: _score(ws_bytes=small, raw=None)) == L.TRIA_EWORKSPACE
     # a paged view whose block table cannot cover n_max slots
     paged = _view(block_table=A, block_size=16, max_blocks=10, n_pool_blocks=100)
     assert _status(lambda: _score(k=paged)) == L.TRIA_ESHAPE

@@ -168,10 +168,12 @@ def _nonconc_unit(cfg):
     return int(rows[0]) if rows.size else 0
 
 
-@pytest.mark.parametrize("name", list(FULL_SAMPLES))
-def test_full_size_sampled_units(name):
+@pytest.mark.parametrize("name,keep_raw", [(n, False) for n in FULL_SAMPLES] + [("qwen3_8b", True)])
+def test_full_size_sampled_units(name, keep_raw):
+    """keep_raw=False is the benchmark's launch configuration (no per-query-head
+    scores written); keep_raw=True also checks those scores at full size."""
     cfg = C[name]
-    prob = _run(cfg)
+    prob = _run(cfg, keep_raw=keep_raw)
     assert prob.flags() == 0
     samples = list(FULL_SAMPLES[name])
     if name == "qwen3_32b":
