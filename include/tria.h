@@ -119,10 +119,10 @@ typedef struct tria_kv_view {
                                  against it on the device                       */
 } tria_kv_view;
 
-/* Bytes of workspace tria_score needs for `n_units` units of at most `n_max`
- * slots (tria_select needs none; given one, it records device flags in it).  The first 256 bytes hold the device flag word: zero them once
- * before first use (tria_device_flags clears them on every read).  Returns 0 for
- * invalid parameters. */
+/* Bytes of workspace tria_score and tria_select need for `n_units` units of at
+ * most `n_max` slots.  The first 256 bytes hold the device flag word: zero them
+ * once before first use (tria_device_flags clears them on every read).  Returns 0
+ * for invalid parameters. */
 size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max);
 
 /* tria_score - the offset-averaged TriAttention score, z-normalised and
@@ -172,6 +172,10 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
 
 /* tria_select - keep the top-B slots of each (unit, KV head)
  * ("Sort. Keep the top-B. Drop the rest." [Blog, The Method]).
+ *
+ * Runs after tria_score on the same stream, with the same workspace, parameters,
+ * n_units and n_max, and on the agg it produced: tria_score leaves a histogram of
+ * the aggregates in the workspace and the selection starts from it.
  *
  * Keeps K_u = min(budget[u], len[u]) slots per (u, g): the slots with the
  * largest agg (protected slots carry +inf, so they are kept whenever

@@ -132,13 +132,14 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 
 // ------------------------------------------------------------------ workspace
 struct Layout {
-  size_t C, N, part, arrive, total;
-  int32_t n_tiles;
+  size_t C, N, part, arrive, hist, st, tiles, list, total;
+  int32_t n_tiles, n_st;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [flag word | coefficients C | norm weights N | tile moments | arrival counters]
+// Workspace: [flag word | coefficients C | norm weights N | tile moments | arrival
+// counters | aggregate histograms | selection state | per-tile counts | candidates]
 Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   Layout L{};
   const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
@@ -153,6 +154,17 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   off += al256(U * hq * (size_t)L.n_tiles * 3 * 8);
   L.arrive = off;
   off += al256(U * (size_t)p->n_kv_heads * 4 + 4);  // + the tile claim counter
+  L.hist = off;
+  off += al256(U * (size_t)p->n_kv_heads * tria::kBins * 4);
+  // selection: per-group state, per-tile counts, candidate lists
+  const size_t ug = U * (size_t)p->n_kv_heads;
+  L.n_st = (n_max + tria::kSelTile - 1) / tria::kSelTile;
+  L.st = off;
+  off += al256(ug * sizeof(tria::SelState));
+  L.tiles = off;
+  off += al256(ug * (size_t)L.n_st * 4 * 3);
+  L.list = off;
+  off += al256(ug * (size_t)n_max * 4);
   L.total = off;
   return L;
 }
@@ -200,6 +212,7 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   double* part = reinterpret_cast<double*>(w + L.part);
   int32_t* arrive = reinterpret_cast<int32_t*>(w + L.arrive);
   int32_t* next_tile = arrive + (size_t)n_units * p->n_kv_heads;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(w + L.hist);
 
   tria::Offsets offs{};
   offs.n = p->n_offsets;
@@ -207,13 +220,13 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
 
   tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->n_kv_heads, p->head_dim, p->n_layers, p->pairing,
                     std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, C, N,
-                    arrive, next_tile, flags};
+                    arrive, next_tile, hist, flags};
   hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
                      tria::score_tile_keys(p->group), L.n_tiles, p->agg,
-                     len, C, N, raw, part, agg, arrive, next_tile, flags};
+                     len, C, N, raw, part, agg, arrive, next_tile, hist, flags};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, s); });
   return launch_status(e, "k_score");
 }
@@ -225,11 +238,24 @@ tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, in
   if (st != TRIA_OK) return st;
   if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
   if (!len || !budget || !agg || !idx || !cnt) return fail(TRIA_EINVAL, "a required device pointer is NULL");
-  if (ws && ws_bytes < 256) return fail(TRIA_EWORKSPACE, "workspace %zu bytes < 256", ws_bytes);
+  if (n_max % 16 != 0) return fail(TRIA_ESHAPE, "n_max %d must be a multiple of 16", n_max);
+  if (reinterpret_cast<uintptr_t>(agg) % 16) return fail(TRIA_ESHAPE, "agg must be 16-byte aligned");
+  if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL (tria_select reads tria_score's histograms from it)");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(TRIA_EWORKSPACE, "workspace must be 256-byte aligned");
+  const Layout L = layout(p, n_units, n_max);
+  if (ws_bytes < L.total)
+    return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if (n_units == 0) return TRIA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, len, budget, agg, idx, cnt,
-                      static_cast<int32_t*>(ws)};
+  char* w = static_cast<char*>(ws);
+  if (L.n_st > tria::kMaxSelTiles)
+    return fail(TRIA_ESHAPE, "n_max %d exceeds the selection's %d tiles", n_max, tria::kMaxSelTiles);
+  int32_t* tiles = reinterpret_cast<int32_t*>(w + L.tiles);
+  const size_t nt = (size_t)n_units * p->n_kv_heads * L.n_st;
+  tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, L.n_st, len, budget, agg,
+                      reinterpret_cast<const uint32_t*>(w + L.hist), reinterpret_cast<tria::SelState*>(w + L.st),
+                      tiles, tiles + nt, tiles + 2 * nt, reinterpret_cast<int32_t*>(w + L.list), idx, cnt,
+                      reinterpret_cast<int32_t*>(w)};
   hipError_t e = timed(kIdSelect, s, [&] { return tria::launch_select(sa, s); });
   return launch_status(e, "k_select");
 }

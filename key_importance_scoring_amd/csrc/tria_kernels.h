@@ -12,8 +12,10 @@ constexpr int kMaxGroup = 8;
 constexpr int kScoreTileMax = 2048;
 // keys per score tile: two tiles of scores ([G][tile + 16] fp32 each) live in LDS
 inline int score_tile_keys(int group) { return group <= 4 ? 2048 : 1024; }
-constexpr int kSpinLimit = 1 << 19;  // bounded wait for a group's tile moments (~0.1 s)
-constexpr int kSelectThreads = 1024;
+constexpr int kSpinLimit = 1 << 19;
+// Linear bins of an aggregate (a z-score: scale-free): 2048 bins over [-8, 8), one
+// below, one above, one for +inf (protected slots).
+constexpr int kBins = 2052;  // bounded wait for a group's tile moments (~0.1 s)
 
 // A cache view with element strides (bf16 elements).
 struct KView {
@@ -50,6 +52,7 @@ struct CoefArgs {
   float* N;                   // [U][Hq][d/2]
   int32_t* arrive;            // [U][Hkv] arrival counters of k_score, cleared here
   int32_t* next_tile;         // tile claim counter of k_score, cleared here
+  uint32_t* hist;             // [U][Hkv][kBins] aggregate histograms of k_score, cleared here
   int32_t* flags;
 };
 
@@ -64,17 +67,39 @@ struct ScoreArgs {
   float* agg;                 // [U][Hkv][n_max]
   int32_t* arrive;            // [U][Hkv] tiles that have published their moments
   int32_t* next_tile;         // next tile to claim
+  uint32_t* hist;             // [U][Hkv][kBins] histogram of the aggregates' linear bins
   int32_t* flags;
 };
 
+// Per-(unit, KV head) state of the selection, in the workspace.
+struct SelState {
+  int32_t b1;    // linear bin holding the K-th largest aggregate (-1: keep all; kBins: keep none)
+  int32_t krem;  // slots still to take from bin b1
+  int32_t K;     // slots kept
+  int32_t n;     // cached slots
+  int32_t m;     // candidates (slots of bin b1) listed
+  int32_t T;     // threshold order key
+  int32_t keq;   // slots equal to T that are kept
+  int32_t pad;
+};
+
+constexpr int kSelTile = 2048;          // slots per selection tile (8 per thread)
+constexpr int kMaxSelTiles = 2048;      // per (unit, KV head): n_max <= 4M
+
 struct SelectArgs {
-  int32_t n_units, n_max, b_max, hkv, sink, window;
+  int32_t n_units, n_max, b_max, hkv, sink, window, n_st;
   const int32_t* len;
   const int32_t* budget;
   const float* agg;
+  const uint32_t* hist;       // [U][Hkv][kBins] binned aggregates, from k_score
+  SelState* st;               // [U][Hkv]
+  int32_t* tile_gt;           // [U][Hkv][n_st] slots above b1 per tile
+  int32_t* tile_off;          // [U][Hkv][n_st] output offset per tile
+  int32_t* tile_eqb;          // [U][Hkv][n_st] tied slots kept per tile
+  int32_t* list;              // [U][Hkv][n_max] candidate slots (bin b1)
   int32_t* idx;               // [U][Hkv][b_max]
   int32_t* cnt;               // [U]
-  int32_t* flags;             // may be null
+  int32_t* flags;
 };
 
 struct CompactArgs {

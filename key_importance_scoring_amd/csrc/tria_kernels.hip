@@ -74,6 +74,16 @@ __device__ inline void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) 
   lo = pack_bf16(a - bf_lo(hi), b - bf_hi(hi));
 }
 
+// Linear bin of an aggregate: monotone non-decreasing in x, so a slot in a higher
+// bin always ranks above a slot in a lower one (NaN, outside the contract, -> 0).
+__device__ inline int lin_bin(float x) {
+  if (!(x == x)) return 0;
+  if (x == __builtin_inff()) return kBins - 1;
+  if (x >= 8.0f) return kBins - 2;
+  if (x < -8.0f) return 0;
+  return 1 + (int)((x + 8.0f) * 128.0f);  // [1, 2048]
+}
+
 template <class V>
 __device__ inline const uint16_t* row_ptr(const V& v, int u, int g, int slot, int32_t* flags) {
   if (v.bt == nullptr)
@@ -102,7 +112,11 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   __shared__ double tw_re[256], tw_im[256];
   __shared__ double rot_re[128], rot_im[128];
 
-  if (blockIdx.y == 0 && t < a.hkv) a.arrive[(size_t)u * a.hkv + t] = 0;
+  if (blockIdx.y == 0) {
+    if (t < a.hkv) a.arrive[(size_t)u * a.hkv + t] = 0;
+    uint32_t* h = a.hist + (size_t)u * a.hkv * kBins;
+    for (int i = t; i < a.hkv * kBins; i += 256) h[i] = 0u;
+  }
   if (u == 0 && blockIdx.y == 0 && t == 0) *a.next_tile = 0;
 
   // statistics of this thread's (query head, band), loaded while the twiddles are formed
@@ -480,7 +494,7 @@ __device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float
 // GQA group onto the KV head [Fold note, sec. 4: normalize-then-max; mean is the
 // other variant] and writes the aggregate; protected slots (sinks, recent window)
 // get +inf.
-__device__ inline void finalize_tile(const ScoreArgs& a, const TileInfo& ti, const float* s_raw) {
+__device__ inline void finalize_tile(const ScoreArgs& a, const TileInfo& ti, const float* s_raw, uint32_t* s_hist) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = a.group;
@@ -523,6 +537,7 @@ __device__ inline void finalize_tile(const ScoreArgs& a, const TileInfo& ti, con
       s_inv[h] = (float)(1.0 / fmax(sqrt(var), 1e-12));
     }
   }
+  for (int i = threadIdx.x; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
 
   const int tlen = ti.tlen, tile0 = ti.tile0, n = ti.n;
@@ -552,6 +567,16 @@ __device__ inline void finalize_tile(const ScoreArgs& a, const TileInfo& ti, con
     } else {
       for (int t = 0; t < 4 && i + t < tlen; ++t) dst[i + t] = out[t];
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (i + t < tlen) atomicAdd(&s_hist[lin_bin(out[t])], 1u);
+  }
+  // the tile's bins join the (unit, KV head) histogram the selection starts from
+  __syncthreads();
+  uint32_t* gh = a.hist + (size_t)ti.ug * kBins;
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    const uint32_t c = s_hist[i];
+    if (c) __hip_atomic_fetch_add(gh + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -582,24 +607,37 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
     const int t = s_t;
     __syncthreads();
     if (t < total) score_phase<D, P, PAGED>(a, tile_info(a, t, true), b ? buf1 : buf0, s_bt);
-    if (prev >= 0) finalize_tile(a, tile_info(a, prev, false), b ? buf0 : buf1);
+    // s_bt served the current tile's score phase; finalize reuses it as histogram scratch
+    if (prev >= 0) finalize_tile(a, tile_info(a, prev, false), b ? buf0 : buf1, reinterpret_cast<uint32_t*>(s_bt));
     if (t >= total) break;
     prev = t;
     b = !b;
   }
 }
 
-// ============================================================================ k_select
+// ============================================================================ selection
+// tria_select keeps, per (unit, KV head), the K = min(B, n) slots with the largest
+// aggregates (ties to the lower slot), in four steps; the two tile-parallel steps
+// carry all the per-slot work, the per-group steps touch only histograms, a short
+// candidate list and per-tile counts:
+//   k_sel_thresh  (per group) the histogram of the aggregates' linear bins, built by
+//                 k_score, gives the bin b1 holding the K-th largest; the binning is
+//                 monotone, so every slot in a higher bin is kept and every slot in a
+//                 lower bin dropped;
+//   k_sel_collect (per tile)  counts the tile's slots above b1 and appends the slots
+//                 of b1 to the group's candidate list;
+//   k_sel_refine  (per group) exact radix passes (11 + 11 + 10 bits of the
+//                 order-preserving key) over the candidates give the threshold key T
+//                 and how many slots equal to T are kept (the lowest ones); then each
+//                 tile's output offset and share of the tied slots;
+//   k_sel_emit    (per tile)  writes the tile's kept slots in ascending order.
 __device__ inline uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);  // -0 -> +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ inline uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// Inclusive prefix sum over the 1024 threads of the workgroup.
+// Inclusive prefix sum over a workgroup of NT threads (wtot: NT / 64 slots).
+template <int NT>
 __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -615,12 +653,41 @@ __device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) {
   return v + base;
 }
 
-__global__ __launch_bounds__(kSelectThreads) void k_select(SelectArgs a) {
+// The bin whose cumulative count from the top first reaches krem (1 <= krem <=
+// total), and the count strictly above it.
+template <int NT>
+__device__ inline void find_digit(const uint32_t* hist, int nb, uint32_t krem, uint32_t* wtot, uint32_t* sh,
+                                  uint32_t& digit, uint32_t& above) {
+  const int c = (nb + NT - 1) / NT;
+  const int top = nb - 1 - (int)threadIdx.x * c;  // this thread's bins: top, top-1, ..., top-c+1
+  uint32_t local = 0;
+  for (int i = 0; i < c; ++i)
+    if (top - i >= 0) local += hist[top - i];
+  const uint32_t incl = block_scan_incl<NT>(local, wtot);
+  const uint32_t excl = incl - local;
+  if (excl < krem && krem <= incl) {
+    uint32_t acc = excl;
+    for (int i = 0; i < c && top - i >= 0; ++i) {
+      const uint32_t h = hist[top - i];
+      if (acc + h >= krem) {
+        sh[0] = (uint32_t)(top - i);
+        sh[1] = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+  digit = sh[0];
+  above = sh[1];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_sel_thresh(SelectArgs a) {
   const int ug = blockIdx.x;
   const int u = ug / a.hkv;
   const int g = ug % a.hkv;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int n = clamp_len(a.len, u, a.n_max, g == 0 ? a.flags : nullptr);
   int B = a.budget[u];
   const int prot = min(n, a.sink + a.window);
@@ -633,91 +700,225 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(SelectArgs a) {
     if (g == 0 && tid == 0) raise_flag(a.flags, kFlagBmax);
     K = a.b_max;
   }
-  const float* v = a.agg + ((size_t)u * a.hkv + g) * a.n_max;
-  int32_t* out = a.idx + ((size_t)u * a.hkv + g) * a.b_max;
   if (g == 0 && tid == 0) a.cnt[u] = K;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t sh[2];
+  int b1;
+  uint32_t krem = 0;
+  if (K == 0) {
+    b1 = kBins;       // no bin is above it: nothing kept
+  } else if (K >= n) {
+    b1 = -1;          // every bin is above it: everything kept
+  } else {
+    const uint32_t* gh = a.hist + (size_t)ug * kBins;
+    for (int i = tid; i < kBins; i += 256) hist[i] = gh[i];
+    __syncthreads();
+    uint32_t d, above;
+    find_digit<256>(hist, kBins, (uint32_t)K, wtot, sh, d, above);
+    b1 = (int)d;
+    krem = (uint32_t)K - above;
+  }
+  if (tid == 0) {
+    SelState& st = a.st[ug];
+    st.b1 = b1;
+    st.krem = (int32_t)krem;
+    st.K = K;
+    st.n = n;
+    st.m = 0;
+    st.T = 0;
+    st.keq = 0;
+  }
+}
 
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wtot[16], wg[16], we[16];
-  __shared__ uint32_t sh_digit, sh_above;
+// Loads the 8 slots [s0, s0 + 8) of a row (two 16-byte loads; s0 < n <= n_max and
+// n_max a multiple of 16, so the loads stay inside the row).
+__device__ inline void load8(const float* row, int s0, float (&x)[8]) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(row + s0);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(row + s0 + 4);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[k] = lo[k];
+    x[k + 4] = hi[k];
+  }
+}
 
-  const bool keep_all = K >= n;
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t krem = (uint32_t)K;
-  if (!keep_all && K > 0) {
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = shifts[pass];
-      const uint32_t nb = 1u << widths[pass];
-      for (int i = tid; i < 2048; i += kSelectThreads) hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelectThreads) {
-        const uint32_t key = order_key(v[i]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
+__global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
+  const int ug = blockIdx.x / a.n_st;
+  const int j = blockIdx.x % a.n_st;
+  const int u = ug / a.hkv;
+  const int tid = threadIdx.x;
+  const SelState st = a.st[ug];
+  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t s_base;
+  const int s0 = j * kSelTile + 8 * tid;
+  uint32_t cgt = 0, cm = 0;
+  float x[8];
+  if (s0 < st.n) {
+    load8(a.agg + ((size_t)u * a.hkv + (ug % a.hkv)) * a.n_max, s0, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < st.n) {
+        const int bin = lin_bin(x[k]);
+        cgt += bin > st.b1 ? 1u : 0u;
+        cm += bin == st.b1 ? 1u : 0u;
       }
-      __syncthreads();
-      // thread t owns bins nb-1-2t and nb-2-2t (descending): find the digit whose
-      // cumulative count from the top first reaches krem
-      const int b0 = (int)nb - 1 - 2 * tid, b1 = b0 - 1;
-      const uint32_t c0 = b0 >= 0 ? hist[b0] : 0u, c1 = b1 >= 0 ? hist[b1] : 0u;
-      const uint32_t incl = block_scan_incl(c0 + c1, wtot);
-      const uint32_t excl = incl - c0 - c1;
-      if (excl < krem && krem <= incl) {
-        if (excl + c0 >= krem) {
-          sh_digit = (uint32_t)b0;
-          sh_above = excl;
-        } else {
-          sh_digit = (uint32_t)b1;
-          sh_above = excl + c0;
-        }
-      }
-      __syncthreads();
-      prefix |= sh_digit << sh;
-      pmask |= (nb - 1) << sh;
-      krem -= sh_above;
-      __syncthreads();
     }
   }
-  // emission in ascending slot order: keep key > T, and the first krem slots with key == T
-  const uint32_t T = prefix;
-  const uint32_t keq = krem;
-  uint32_t gt_base = 0, eq_base = 0;
-  if (K > 0) {
-    for (int base = 0; base < n; base += kSelectThreads) {
-      const int i = base + tid;
-      const bool valid = i < n;
-      const uint32_t key = valid ? order_key(v[i]) : 0u;
-      const bool gt = valid && (keep_all || key > T);
-      const bool eq = valid && !keep_all && key == T;
-      const uint64_t bg = __ballot(gt), be = __ballot(eq);
-      if (lane == 0) {
-        wg[wave] = (uint32_t)__popcll(bg);
-        we[wave] = (uint32_t)__popcll(be);
+  const uint32_t gt_tot = block_scan_incl<256>(cgt, wtot);
+  const uint32_t m_incl = block_scan_incl<256>(cm, wtot);
+  if (tid == 255) {
+    a.tile_gt[blockIdx.x] = (int32_t)gt_tot;
+    s_base = m_incl ? (uint32_t)atomicAdd(&a.st[ug].m, (int32_t)m_incl) : 0u;
+  }
+  __syncthreads();
+  if (cm) {
+    int32_t* list = a.list + (size_t)ug * a.n_max;
+    uint32_t pos = s_base + m_incl - cm;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < st.n && lin_bin(x[k]) == st.b1 && pos < (uint32_t)a.n_max) list[pos++] = s0 + k;
+  }
+}
+
+__global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
+  const int ug = blockIdx.x;
+  const int u = ug / a.hkv;
+  const int tid = threadIdx.x;
+  const SelState st = a.st[ug];
+  const float* row = a.agg + ((size_t)u * a.hkv + (ug % a.hkv)) * a.n_max;
+  const int32_t* list = a.list + (size_t)ug * a.n_max;
+  const int m = min(st.m, a.n_max);
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wtot[8];
+  __shared__ uint32_t sh[2];
+  __shared__ int32_t s_gtb[kMaxSelTiles], s_eqc[kMaxSelTiles];
+
+  uint32_t T = 0, keq = 0;
+  const bool refine = st.b1 >= 0 && st.b1 < kBins;
+  if (refine) {
+    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)st.krem;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sft = pass == 0 ? 21 : (pass == 1 ? 10 : 0);   // digits of 11, 11, 10 bits
+      const int nb = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < nb; i += 512) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < m; i += 512) {
+        const uint32_t key = order_key(row[list[i]]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sft) & (nb - 1)], 1u);
       }
       __syncthreads();
-      uint32_t pg = 0, pe = 0, tg = 0, te = 0;
-      for (int w = 0; w < kSelectThreads / 64; ++w) {
-        const uint32_t x = wg[w], y = we[w];
-        if (w < wave) {
-          pg += x;
-          pe += y;
-        }
-        tg += x;
-        te += y;
+      uint32_t d, ab;
+      find_digit<512>(hist, nb, krem, wtot, sh, d, ab);
+      prefix |= d << sft;
+      pmask |= (uint32_t)(nb - 1) << sft;
+      krem -= ab;
+    }
+    T = prefix;
+    keq = krem;
+  }
+  // per tile: candidates above T and equal to T
+  for (int i = tid; i < a.n_st; i += 512) {
+    s_gtb[i] = 0;
+    s_eqc[i] = 0;
+  }
+  __syncthreads();
+  if (refine) {
+    for (int i = tid; i < m; i += 512) {
+      const int slot = list[i];
+      const uint32_t key = order_key(row[slot]);
+      if (key > T) atomicAdd(&s_gtb[slot / kSelTile], 1);
+      else if (key == T) atomicAdd(&s_eqc[slot / kSelTile], 1);
+    }
+  }
+  __syncthreads();
+  // tied slots are kept lowest first: tile j keeps min(eq_j, keq - eq before j);
+  // output offsets are the prefix sums of the tiles' kept counts
+  const int per = (a.n_st + 511) / 512;
+  const int j0 = tid * per;
+  uint32_t eq_local = 0;
+  for (int i = 0; i < per && j0 + i < a.n_st; ++i) eq_local += (uint32_t)s_eqc[j0 + i];
+  uint32_t eq_before = block_scan_incl<512>(eq_local, wtot) - eq_local;
+  uint32_t kept_local[1] = {0};
+  // first sweep: kept counts (needs eq_before per tile)
+  uint32_t eb = eq_before;
+  for (int i = 0; i < per && j0 + i < a.n_st; ++i) {
+    const int jj = j0 + i;
+    const uint32_t e = (uint32_t)s_eqc[jj];
+    const uint32_t share = eb >= keq ? 0u : min(e, keq - eb);
+    eb += e;
+    kept_local[0] += (uint32_t)a.tile_gt[(size_t)ug * a.n_st + jj] + (uint32_t)s_gtb[jj] + share;
+  }
+  uint32_t off = block_scan_incl<512>(kept_local[0], wtot) - kept_local[0];
+  eb = eq_before;
+  for (int i = 0; i < per && j0 + i < a.n_st; ++i) {
+    const int jj = j0 + i;
+    const uint32_t e = (uint32_t)s_eqc[jj];
+    const uint32_t share = eb >= keq ? 0u : min(e, keq - eb);
+    eb += e;
+    a.tile_off[(size_t)ug * a.n_st + jj] = (int32_t)off;
+    a.tile_eqb[(size_t)ug * a.n_st + jj] = (int32_t)share;
+    off += (uint32_t)a.tile_gt[(size_t)ug * a.n_st + jj] + (uint32_t)s_gtb[jj] + share;
+  }
+  if (tid == 0) {
+    a.st[ug].T = (int32_t)T;
+    a.st[ug].keq = (int32_t)keq;
+  }
+  int32_t* out = a.idx + ((size_t)u * a.hkv + (ug % a.hkv)) * a.b_max;
+  for (int i = st.K + tid; i < a.b_max; i += 512) out[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
+  const int ug = blockIdx.x / a.n_st;
+  const int u = ug / a.hkv;
+  const int tid = threadIdx.x;
+  const SelState st = a.st[ug];
+  const uint32_t T = (uint32_t)st.T;
+  const uint32_t eqb = (uint32_t)a.tile_eqb[blockIdx.x];
+  const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
+  __shared__ uint32_t wtot[4];
+  const int s0 = (blockIdx.x % a.n_st) * kSelTile + 8 * tid;
+  float x[8];
+  uint32_t gtm = 0, eqm = 0;   // per-slot bit masks
+  if (s0 < st.n) {
+    load8(a.agg + ((size_t)u * a.hkv + (ug % a.hkv)) * a.n_max, s0, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < st.n) {
+        const int bin = lin_bin(x[k]);
+        const uint32_t key = order_key(x[k]);
+        const bool gt = bin > st.b1 || (bin == st.b1 && key > T);
+        const bool eq = bin == st.b1 && key == T;
+        gtm |= (gt ? 1u : 0u) << k;
+        eqm |= (eq ? 1u : 0u) << k;
       }
-      const uint32_t gb = gt_base + pg + lanes_below(bg);
-      const uint32_t eb = eq_base + pe + lanes_below(be);
+    }
+  }
+  // tied slots of this tile are kept lowest first, up to its share eqb
+  const uint32_t ne = (uint32_t)__popc(eqm);
+  const uint32_t eq_before = block_scan_incl<256>(ne, wtot) - ne;
+  uint32_t keep = gtm;
+  uint32_t r = eq_before;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if ((eqm >> k) & 1u) {
+      if (r < eqb) keep |= 1u << k;
+      ++r;
+    }
+  }
+  const uint32_t nk = (uint32_t)__popc(keep);
+  uint32_t pos = off + block_scan_incl<256>(nk, wtot) - nk;
+  int32_t* out = a.idx + ((size_t)u * a.hkv + (ug % a.hkv)) * a.b_max;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if ((keep >> k) & 1u) {
       // positions are < K by construction; the bound keeps a miscount from ever
       // writing past the caller's b_max row
-      const uint32_t pos = gb + (eb < keq ? eb : keq);
-      if ((gt || (eq && eb < keq)) && pos < (uint32_t)K) out[pos] = i;
-      gt_base += tg;
-      eq_base += te;
-      __syncthreads();
+      if (pos < (uint32_t)st.K) out[pos] = s0 + k;
+      ++pos;
     }
   }
-  for (int j = K + tid; j < a.b_max; j += kSelectThreads) out[j] = -1;
 }
 
 // ============================================================================ k_compact
@@ -772,7 +973,10 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
 
 size_t score_lds(int group, bool paged) {
   const int tile = score_tile_keys(group);
-  return (size_t)2 * group * (tile + 16) * 4 + (paged ? (size_t)(tile + 1) * 4 : 0);
+  // two score buffers, then a region that holds the tile's block ids during the
+  // score phase and the aggregate histogram during finalisation
+  const size_t scratch = paged && tile + 1 > kBins ? (size_t)tile + 1 : (size_t)kBins;
+  return (size_t)2 * group * (tile + 16) * 4 + scratch * 4;
 }
 
 int score_capacity(int d, int pairing, bool paged, int group) {
@@ -831,9 +1035,17 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const long blocks = (long)a.n_units * a.hkv;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_select, dim3((unsigned)blocks), dim3(kSelectThreads), 0, s, a);
+  const long groups = (long)a.n_units * a.hkv;
+  if (groups == 0) return hipSuccess;
+  const unsigned tiles = (unsigned)(groups * a.n_st);
+  hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sel_refine, dim3((unsigned)groups), dim3(512), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sel_emit, dim3(tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

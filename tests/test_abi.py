@@ -142,15 +142,20 @@ def test_score_shape_and_workspace_checks():
 def test_zero_units_is_a_no_op():
     # returns OK without launching anything (no GPU here)
     _score(n_units=0)
-    L.tria_select(_params(), 0, 4096, 16, A, A, A, A, A)
+    L.tria_select(_params(), 0, 4096, 16, A, A, A, A, A, WS, L.tria_workspace_size(_params(), 0, 4096))
 
 
 def test_select_checks():
     p = _params()
-    assert _status(lambda: L.tria_select(p, 2, 4096, 16, None, A, A, A, A)) == L.TRIA_EINVAL
-    assert _status(lambda: L.tria_select(p, 2, 4096, -1, A, A, A, A, A)) == L.TRIA_EINVAL
+    need = L.tria_workspace_size(p, 2, 4096)
+    assert _status(lambda: L.tria_select(p, 2, 4096, 16, None, A, A, A, A, WS, need)) == L.TRIA_EINVAL
+    assert _status(lambda: L.tria_select(p, 2, 4096, -1, A, A, A, A, A, WS, need)) == L.TRIA_EINVAL
     assert _status(lambda: L.tria_select(p, 2, 4096, 16, A, A, A, A, A, WS, 100)) == L.TRIA_EWORKSPACE
-    assert _status(lambda: L.tria_select(_params(agg=3), 2, 4096, 16, A, A, A, A, A)) == L.TRIA_EINVAL
+    assert _status(lambda: L.tria_select(p, 2, 4096, 16, A, A, A, A, A, None, 0)) == L.TRIA_EWORKSPACE
+    assert _status(lambda: L.tria_select(p, 2, 4096, 16, A, A, A, A, A, WS + 64, need)) == L.TRIA_EWORKSPACE
+    assert _status(lambda: L.tria_select(p, 2, 4100, 16, A, A, A, A, A, WS, need)) == L.TRIA_ESHAPE
+    assert _status(lambda: L.tria_select(p, 2, 4096, 16, A, A, A + 4, A, A, WS, need)) == L.TRIA_ESHAPE
+    assert _status(lambda: L.tria_select(_params(agg=3), 2, 4096, 16, A, A, A, A, A, WS, need)) == L.TRIA_EINVAL
 
 
 def _compact(k_src, v_src, k_dst, v_dst, pos_src=None, pos_dst=None, pos_heads=1, n_units=2, n_max=4096, b_max=2048):
