@@ -106,7 +106,10 @@ typedef struct tria_params {
  *   dense : base + u*stride_unit + g*stride_head + i*stride_slot
  *   paged : base + (bt[u*max_blocks + i/block_size]*block_size + i%block_size)
  *                  * stride_slot + g*stride_head
- * (strides in bf16 elements, each a multiple of 8; base 16-byte aligned).  */
+ * (strides in bf16 elements, each a multiple of 8; base 16-byte aligned).
+ * tria_score may read (and ignore) rows of slots in [len[u], n_max): a dense view
+ * must be readable for every slot below n_max, and a paged view's table must
+ * cover n_max slots (its ids past len[u] may be anything, -1 included).  */
 typedef struct tria_kv_view {
   void* base;                 /* [device] bf16 rows                             */
   int64_t stride_unit;        /* dense only                                     */

@@ -132,28 +132,26 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 
 // ------------------------------------------------------------------ workspace
 struct Layout {
-  size_t C, N, part, arrive, hist, st, tiles, list, total;
+  size_t B, part, claim, hist, st, tiles, list, total;
   int32_t n_tiles, n_st;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [flag word | coefficients C | norm weights N | tile moments | arrival
-// counters | aggregate histograms | selection state | per-tile counts | candidates]
+// Workspace: [flag word | MFMA B operands | tile moments | tile
+// claim counter | aggregate histograms | selection state | per-tile counts | candidates]
 Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   Layout L{};
   const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
   const int tile = tria::score_tile_keys(p->group);
   L.n_tiles = (n_max + tile - 1) / tile;
   size_t off = 256;  // flag word
-  L.C = off;
-  off += al256(U * hq * d * 4);
-  L.N = off;
-  off += al256(U * hq * (d / 2) * 4);
+  L.B = off;
+  off += al256(U * (size_t)p->n_kv_heads * (d / 16) * 64 * 16);  // MFMA B operands, 16 B per lane
   L.part = off;
   off += al256(U * hq * (size_t)L.n_tiles * 3 * 8);
-  L.arrive = off;
-  off += al256(U * (size_t)p->n_kv_heads * 4 + 4);  // + the tile claim counter
+  L.claim = off;
+  off += 256;  // the tile claim counter
   L.hist = off;
   off += al256(U * (size_t)p->n_kv_heads * tria::kBins * 4);
   // selection: per-group state, per-tile counts, candidate lists
@@ -207,11 +205,9 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   char* w = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* flags = reinterpret_cast<int32_t*>(w);
-  float* C = reinterpret_cast<float*>(w + L.C);
-  float* N = reinterpret_cast<float*>(w + L.N);
+  uint32_t* B = reinterpret_cast<uint32_t*>(w + L.B);
   double* part = reinterpret_cast<double*>(w + L.part);
-  int32_t* arrive = reinterpret_cast<int32_t*>(w + L.arrive);
-  int32_t* next_tile = arrive + (size_t)n_units * p->n_kv_heads;
+  int32_t* next_tile = reinterpret_cast<int32_t*>(w + L.claim);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + L.hist);
 
   tria::Offsets offs{};
@@ -219,14 +215,14 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   for (int i = 0; i < p->n_offsets; ++i) offs.v[i] = (double)p->offsets[i];
 
   tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->n_kv_heads, p->head_dim, p->n_layers, p->pairing,
-                    std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, C, N,
-                    arrive, next_tile, hist, flags};
+                    std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean,
+                    p->group, L.n_tiles, B, reinterpret_cast<uint64_t*>(part), next_tile, hist, flags};
   hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
                      tria::score_tile_keys(p->group), L.n_tiles, p->agg,
-                     len, C, N, raw, part, agg, arrive, next_tile, hist, flags};
+                     len, B, raw, part, agg, next_tile, hist, flags};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, s); });
   return launch_status(e, "k_score");
 }

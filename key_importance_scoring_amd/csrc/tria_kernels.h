@@ -11,11 +11,20 @@ constexpr int kMaxOffsets = 256;
 constexpr int kMaxGroup = 8;
 constexpr int kScoreTileMax = 2048;
 // keys per score tile: two tiles of scores ([G][tile + 16] fp32 each) live in LDS
-inline int score_tile_keys(int group) { return group <= 4 ? 2048 : 1024; }
-constexpr int kSpinLimit = 1 << 19;
+#ifndef TRIA_SCORE_TILE_SMALL_G
+#define TRIA_SCORE_TILE_SMALL_G 2048
+#endif
+inline int score_tile_keys(int group) { return group <= 4 ? TRIA_SCORE_TILE_SMALL_G : 1024; }
+// A tile's published moments start as this bit pattern (cleared by k_coef): a NaN
+// whose low payload bits are set, which no moment computed from fp32 scores can
+// take (NaNs that arithmetic produces keep an fp32 payload or are the default one).
+constexpr uint64_t kUnpublished = ~0ull;
+// Bounded wait for a group's tile moments: each poll is one memory round trip plus a
+// short sleep (~0.1-0.2 s in all).
+constexpr int kPollLimit = 1 << 16;
 // Linear bins of an aggregate (a z-score: scale-free): 2048 bins over [-8, 8), one
 // below, one above, one for +inf (protected slots).
-constexpr int kBins = 2052;  // bounded wait for a group's tile moments (~0.1 s)
+constexpr int kBins = 2052;
 
 // A cache view with element strides (bf16 elements).
 struct KView {
@@ -48,9 +57,9 @@ struct CoefArgs {
   const float* q_re;
   const float* q_im;
   const float* q_abs;
-  float* C;                   // [U][Hq][d]
-  float* N;                   // [U][Hq][d/2]
-  int32_t* arrive;            // [U][Hkv] arrival counters of k_score, cleared here
+  int32_t group, n_tiles;     // query heads per KV head; score tiles per (unit, KV head)
+  uint32_t* B;                // [U][Hkv][d/16][64] 16-byte MFMA B operands of k_score
+  uint64_t* part;             // [U][Hq][n_tiles][3] tile moments of k_score, set to kUnpublished here
   int32_t* next_tile;         // tile claim counter of k_score, cleared here
   uint32_t* hist;             // [U][Hkv][kBins] aggregate histograms of k_score, cleared here
   int32_t* flags;
@@ -60,12 +69,10 @@ struct ScoreArgs {
   KView k;
   int32_t n_units, n_max, hkv, group, sink, window, tile, n_tiles, agg_mode;
   const int32_t* len;
-  const float* C;
-  const float* N;
+  const uint32_t* B;          // [U][Hkv][d/16][64] 16-byte MFMA B operands, from k_coef
   float* raw;                 // [U][Hq][n_max], may be null
   double* part;               // [U][Hq][n_tiles][3] tile moments (count, sum, sum of squares)
   float* agg;                 // [U][Hkv][n_max]
-  int32_t* arrive;            // [U][Hkv] tiles that have published their moments
   int32_t* next_tile;         // next tile to claim
   uint32_t* hist;             // [U][Hkv][kBins] histogram of the aggregates' linear bins
   int32_t* flags;

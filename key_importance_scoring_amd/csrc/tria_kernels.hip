@@ -50,13 +50,16 @@ __device__ inline void raise_flag(int32_t* flags, int32_t bit) {
   if (flags) atomicOr(flags, bit);
 }
 
-__device__ inline int clamp_len(const int32_t* len, int u, int n_max, int32_t* flags) {
-  int n = len[u];
+__device__ inline int fix_len(int n, int n_max, int32_t* flags) {
   if (n < 0 || n > n_max) {
     raise_flag(flags, kFlagLen);
     n = n < 0 ? 0 : n_max;
   }
   return n;
+}
+
+__device__ inline int clamp_len(const int32_t* len, int u, int n_max, int32_t* flags) {
+  return fix_len(len[u], n_max, flags);
 }
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -96,86 +99,7 @@ __device__ inline const uint16_t* row_ptr(const V& v, int u, int g, int slot, in
   return v.base + ((int64_t)blk * v.bs + slot % v.bs) * v.ss + (int64_t)g * v.sh;
 }
 
-// ============================================================================ k_coef
-// Grid (unit, chunk of 256 (query head, band) pairs).  Per-(band, offset) twiddles
-// e^{i w_f delta} are summed by F x (256/F) threads into LDS partials; W_f and the
-// rotation to q_pos are formed once per band; then each thread forms one (query
-// head, band) coefficient, so the statistics loads of a block are all in flight
-// together.  Block (u, 0) also clears the unit's arrival counters of k_score.
-__global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
-  const int u = blockIdx.x;
-  const int F = a.d / 2;
-  const int t = threadIdx.x;
-  const int subs = 256 / F;
-  const int f = t % F;
-  const int s = t / F;
-  __shared__ double tw_re[256], tw_im[256];
-  __shared__ double rot_re[128], rot_im[128];
-
-  if (blockIdx.y == 0) {
-    if (t < a.hkv) a.arrive[(size_t)u * a.hkv + t] = 0;
-    uint32_t* h = a.hist + (size_t)u * a.hkv * kBins;
-    for (int i = t; i < a.hkv * kBins; i += 256) h[i] = 0u;
-  }
-  if (u == 0 && blockIdx.y == 0 && t == 0) *a.next_tile = 0;
-
-  // statistics of this thread's (query head, band), loaded while the twiddles are formed
-  const int p = blockIdx.y * 256 + t;
-  const int h = p / F, b = p % F;
-  const int layer = a.unit_layer[u];
-  const bool ok = layer >= 0 && layer < a.layers;
-  if (!ok && t == 0 && blockIdx.y == 0) raise_flag(a.flags, kFlagLayer);
-  double mr = 0.0, mi = 0.0, ab = 0.0;
-  if (ok && p < a.hq * F) {
-    const size_t si = ((size_t)layer * a.hq + h) * F + b;
-    mr = a.q_re[si];
-    mi = a.q_im[si];
-    ab = a.q_abs[si];
-  }
-
-  // band frequency w_f = theta^(-2f/d)  [Fold note, sec. 2, Eq. 2 bullets]
-  const double w = exp(-(2.0 * f / a.d) * a.log_base);
-  double cs = 0.0, sn = 0.0;
-  for (int j = s; j < offs.n; j += subs) {
-    double sv, cv;
-    sincos(w * offs.v[j], &sv, &cv);
-    cs += cv;
-    sn += sv;
-  }
-  tw_re[t] = cs;
-  tw_im[t] = sn;
-  __syncthreads();
-  if (t < F) {
-    double wr = 0.0, wi = 0.0;
-    for (int j = 0; j < subs; ++j) {
-      wr += tw_re[j * F + t];
-      wi += tw_im[j * F + t];
-    }
-    wr /= offs.n;  // W_f  [Fold note, Eq. 6]
-    wi /= offs.n;
-    double sv, cv;
-    sincos(w * (double)a.q_pos[u], &sv, &cv);
-    rot_re[t] = wr * cv - wi * sv;  // W_f e^{i w_f q_pos}
-    rot_im[t] = wr * sv + wi * cv;
-  }
-  __syncthreads();
-  if (p >= a.hq * F) return;
-
-  // c = mu' e^{i w q_pos} with mu' = E[q_f] W_f  [Fold note, Eq. 7]
-  const double cr = mr * rot_re[b] - mi * rot_im[b];
-  const double ci = mr * rot_im[b] + mi * rot_re[b];
-  // Re(c conj(k)) = Re(c) Re(k) + Im(c) Im(k): coefficients sit where the key's
-  // real / imaginary parts sit in the pairing layout  [Calib issue, pairing]
-  float* crow = a.C + ((size_t)u * a.hq + h) * a.d;
-  const int ire = a.pairing == 0 ? b : 2 * b;
-  const int iim = a.pairing == 0 ? b + F : 2 * b + 1;
-  crow[ire] = (float)cr;
-  crow[iim] = (float)ci;
-  // norm weight E|q_f| - |E q_f| = E|q_f| (1 - R_f)  [Blog, The Method; reading]
-  a.N[((size_t)u * a.hq + h) * F + b] = (float)(ab - sqrt(mr * mr + mi * mi));
-}
-
-// ============================================================================ k_score
+// ============================================================================ MFMA operand layout
 // MFMA 16x16x32 bf16 layout (gfx950): lane l feeds A row (l & 15) and B column
 // (l & 15) with k-elements [8 (l >> 4), 8 (l >> 4) + 8); it receives D rows
 // 4 (l >> 4) + t, t < 4, of column (l & 15).
@@ -190,7 +114,9 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
 // B columns: 0..G-1 carry the hi part of query head h's coefficients, 8..8+G-1
 // the lo part; one DPP row shift by 8 adds them.  Magnitudes are split hi/lo
 // too; the lo magnitudes meet only hi coefficients (the lo*lo product is below
-// 2^-16 of the term).
+// 2^-16 of the term).  k_coef writes each lane's B operands (coefficients and
+// norm weights, hi/lo split, zero in unused columns) in this order, so that
+// k_score loads them with one coalesced 16-byte load per operand.
 template <int D>
 struct Shape {
   static constexpr int F = D / 2;
@@ -213,6 +139,135 @@ __device__ inline int lane_band(int q, int c) {
   return D / 4 + c * (D / 16) + (q - D / 16);         // interleaved, second half
 }
 
+// ============================================================================ k_coef
+// Grid (unit, KV head).  Per-(band, offset) twiddles e^{i w_f delta} are summed by
+// F x (256/F) threads into LDS partials; W_f and the rotation to q_pos are formed
+// once per band; each (query head, band) of the group then forms its coefficient
+// into LDS, and the block finally writes them as k_score's MFMA B operands, in the
+// order its lanes load them (the MFMA operand layout above).  The block also
+// resets its (unit, KV head)'s tile moments to kUnpublished and clears its
+// aggregate histogram; block (0, 0) clears the tile claim counter.
+template <int D, int P>
+__global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
+  using S = Shape<D>;
+  constexpr int F = D / 2;
+  constexpr int NB = S::NKC + 2 * S::NNC;
+  constexpr int PER = (kMaxGroup * F + 255) / 256;  // (head, band) pairs per thread
+  const int u = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int G = a.group;
+  const int hq = a.hkv * G;
+  const size_t ug = (size_t)u * a.hkv + g;
+  __shared__ double tw_re[256], tw_im[256];
+  __shared__ double rot_re[F], rot_im[F];
+  __shared__ float s_c[kMaxGroup * D];  // coefficient rows, pairing layout
+  __shared__ float s_n[kMaxGroup * F];  // norm weights
+
+  const int64_t per = (int64_t)G * a.n_tiles * 3;
+  for (int64_t i = t; i < per; i += 256) a.part[ug * per + i] = kUnpublished;
+  for (int i = t; i < kBins; i += 256) a.hist[ug * kBins + i] = 0u;
+  if (u == 0 && g == 0 && t == 0) *a.next_tile = 0;
+
+  // statistics of this thread's (query head, band) pairs, loaded while the twiddles are formed
+  const int layer = a.unit_layer[u];
+  const bool ok = layer >= 0 && layer < a.layers;
+  if (!ok && t == 0 && g == 0) raise_flag(a.flags, kFlagLayer);
+  double mr[PER], mi[PER], ab[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int p = t + 256 * k, h = p / F, b = p % F;
+    mr[k] = mi[k] = ab[k] = 0.0;
+    if (ok && h < G) {
+      const size_t si = ((size_t)layer * hq + g * G + h) * F + b;
+      mr[k] = a.q_re[si];
+      mi[k] = a.q_im[si];
+      ab[k] = a.q_abs[si];
+    }
+  }
+
+  // band frequency w_f = theta^(-2f/d)  [Fold note, sec. 2, Eq. 2 bullets]
+  constexpr int subs = 256 / F;
+  const int f = t % F, sub = t / F;
+  const double w = exp(-(2.0 * f / D) * a.log_base);
+  double cs = 0.0, sn = 0.0;
+  for (int j = sub; j < offs.n; j += subs) {
+    double sv, cv;
+    sincos(w * offs.v[j], &sv, &cv);
+    cs += cv;
+    sn += sv;
+  }
+  tw_re[t] = cs;
+  tw_im[t] = sn;
+  __syncthreads();
+  if (t < F) {
+    double wr = 0.0, wi = 0.0;
+    for (int j = 0; j < subs; ++j) {
+      wr += tw_re[j * F + t];
+      wi += tw_im[j * F + t];
+    }
+    wr /= offs.n;  // W_f  [Fold note, Eq. 6]
+    wi /= offs.n;
+    double sv, cv;
+    sincos(w * (double)a.q_pos[u], &sv, &cv);
+    rot_re[t] = wr * cv - wi * sv;  // W_f e^{i w_f q_pos}
+    rot_im[t] = wr * sv + wi * cv;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int p = t + 256 * k, h = p / F, b = p % F;
+    if (h >= G) continue;
+    // c = mu' e^{i w q_pos} with mu' = E[q_f] W_f  [Fold note, Eq. 7]
+    const double cr = mr[k] * rot_re[b] - mi[k] * rot_im[b];
+    const double ci = mr[k] * rot_im[b] + mi[k] * rot_re[b];
+    // Re(c conj(k)) = Re(c) Re(k) + Im(c) Im(k): coefficients sit where the key's
+    // real / imaginary parts sit in the pairing layout  [Calib issue, pairing]
+    s_c[h * D + (P == 0 ? b : 2 * b)] = (float)cr;
+    s_c[h * D + (P == 0 ? b + F : 2 * b + 1)] = (float)ci;
+    // norm weight E|q_f| - |E q_f| = E|q_f| (1 - R_f)  [Blog, The Method; reading]
+    s_n[h * F + b] = (float)(ab[k] - sqrt(mr[k] * mr[k] + mi[k] * mi[k]));
+  }
+  __syncthreads();
+
+  // B operands: operand s of lane l at B[(u, g)][s][l]; s < NKC are the dot part's
+  // chunks, then the norm part's hi-magnitude and lo-magnitude operands
+  u32x4* dst = reinterpret_cast<u32x4*>(a.B) + ug * NB * 64;
+  for (int q = t; q < NB * 64; q += 256) {
+    const int s = q / 64, lane = q % 64;
+    const int col = lane & 15, grp = lane >> 4;
+    int head = -1;
+    bool lo = false;
+    if (col < G) head = col;
+    else if (col >= 8 && col < 8 + G) { head = col - 8; lo = true; }
+    u32x4 w4 = {0u, 0u, 0u, 0u};
+    if (head >= 0) {
+      if (s < S::NKC) {
+        const int e0 = chunk_elem<D>(s, grp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t hi, lw;
+          split_bf16(s_c[head * D + e0 + 2 * j], s_c[head * D + e0 + 2 * j + 1], hi, lw);
+          w4[j] = lo ? lw : hi;
+        }
+      } else {
+        const int i = (s - S::NKC) % S::NNC;
+        const bool second = s >= S::NKC + S::NNC;  // the operand that meets lo magnitudes
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = s_n[head * F + lane_band<D, P>(8 * i + 2 * j, grp)];
+          const float x1 = s_n[head * F + lane_band<D, P>(8 * i + 2 * j + 1, grp)];
+          uint32_t hi, lw;
+          split_bf16(x0, x1, hi, lw);
+          w4[j] = second ? (lo ? 0u : hi) : (lo ? lw : hi);
+        }
+      }
+    }
+    dst[s * 64 + lane] = w4;
+  }
+}
+
+
+// ============================================================================ k_score
 // re^2 + im^2 of a packed bf16 pair (re in the low half), products exact in fp32.
 // Kept as the builtin (not hand-written asm) so the compiler sees the instruction
 // and inserts the wait states its consumers (v_sqrt) need.
@@ -244,6 +299,11 @@ __device__ inline float band_sq(const u32x4 (&ch)[D / 32], int q) {
 // 16-key blocks per pipeline stage (d = 256 rows are twice as large: half as many)
 template <int D>
 constexpr int stage_blocks() { return D >= 256 ? (TRIA_SCORE_NBI + 1) / 2 : TRIA_SCORE_NBI; }
+// a wave's keys (tile / 4, tiles of 1024 or 2048) must be whole stages: a stage's
+// scores are written to LDS for all its keys, and a partial last stage would write
+// into the next wave's range
+static_assert((1024 / 4) % (16 * stage_blocks<64>()) == 0 && (1024 / 4) % (16 * stage_blocks<256>()) == 0,
+              "stage size must divide a wave's keys");
 
 // One pipeline stage of a wave: stage_blocks blocks of 16 keys, d/32 16-byte chunks per lane each.
 template <int D>
@@ -251,7 +311,7 @@ using Stage = u32x4[stage_blocks<D>()][D / 32];
 
 // Issues the loads of one stage.  Keys at or past `kend` (the end of the wave's
 // range) are clamped to its last key, whose row is already in cache: their scores
-// are computed but never stored or counted.  Every load is unconditional, so the
+// are computed but never counted.  Every load is unconditional, so the
 // compiler can keep the next stage in flight while the current one computes.
 template <int D, bool PAGED>
 __device__ inline void load_stage(Stage<D>& ch, const KView& k, int u, int g, int kb, int kend, int col, int grp,
@@ -263,7 +323,8 @@ __device__ inline void load_stage(Stage<D>& ch, const KView& k, int u, int g, in
     if (!PAGED) {
       rp = k.base + (int64_t)u * k.su + (int64_t)g * k.sh + (int64_t)key * k.ss;
     } else {
-      const int blk = s_bt[key / k.bs - page0];
+      const int b0 = s_bt[key / k.bs - page0];
+      const int blk = b0 >= 0 && b0 < k.npb ? b0 : 0;
       rp = k.base + ((int64_t)blk * k.bs + key % k.bs) * k.ss + (int64_t)g * k.sh;
     }
 #pragma unroll
@@ -276,22 +337,28 @@ struct TileInfo {
   int ug, u, g, tile, n, tile0, tlen;
 };
 
-__device__ inline TileInfo tile_info(const ScoreArgs& a, int t, bool flag) {
+// The tile's place; its length fields are filled by tile_len, which loads len[u]
+// (kept apart so that a tile's first loads need not wait for it).
+__device__ inline TileInfo tile_info(const ScoreArgs& a, int t) {
   TileInfo ti;
   ti.tile = t % a.n_tiles;
   ti.ug = t / a.n_tiles;
   ti.u = ti.ug / a.hkv;
   ti.g = ti.ug % a.hkv;
-  ti.n = clamp_len(a.len, ti.u, a.n_max, flag && threadIdx.x == 0 ? a.flags : nullptr);
   ti.tile0 = ti.tile * a.tile;
-  ti.tlen = max(0, min(a.tile, ti.n - ti.tile0));
+  ti.n = ti.tlen = 0;
   return ti;
+}
+
+__device__ inline void tile_len(const ScoreArgs& a, TileInfo& ti, int n_loaded, bool flag) {
+  ti.n = fix_len(n_loaded, a.n_max, flag && threadIdx.x == 0 ? a.flags : nullptr);
+  ti.tlen = max(0, min(a.tile, ti.n - ti.tile0));
 }
 
 // Scores one tile into LDS (s_raw, [G][tile + 16]), writes the per-query-head
 // scores if wanted, and publishes the tile's candidate moments.
 template <int D, int P, bool PAGED>
-__device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float* s_raw, int* s_bt) {
+__device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, float* s_raw, int* s_bt) {
   using S = Shape<D>;
   constexpr int NBI = stage_blocks<D>();
   constexpr int STAGE = 16 * NBI;  // keys per pipeline stage
@@ -303,70 +370,56 @@ __device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float
   const int hq = a.hkv * G;
   const int RS = a.tile + 16;      // LDS row stride: heads start 16 banks apart
   const int kpw = a.tile / 4;      // keys per wave
-  const int u = ti.u, g = ti.g, n = ti.n, tile0 = ti.tile0;
+  const int u = ti.u, g = ti.g, tile0 = ti.tile0;
+  const int kw0 = tile0 + wave * kpw;
+  // slots whose rows exist whatever len[u] is (a dense view is readable, and a paged
+  // view's table covers, n_max slots): the first stage is issued before len[u] arrives
+  const int kcap = min(kw0 + kpw, a.n_max);
+  const int n_loaded = a.len[u];   // first needed once the first two stages are in flight
 
-  // ---- paged caches: the tile's block ids, checked once, in LDS
+  // ---- paged caches: the tile's block ids in LDS.  Ids of pages past len[u] may be
+  // anything: load_stage maps an out-of-pool id to block 0, and only pages that
+  // hold cached slots are checked (below)
   int page0 = 0;
   if (PAGED) {
     page0 = tile0 / a.k.bs;
-    const int last = min(tile0 + a.tile, n) - 1;
-    const int npages = last >= tile0 ? last / a.k.bs - page0 + 1 : 0;
-    for (int i = threadIdx.x; i < npages; i += 256) {
-      int blk = a.k.bt[(int64_t)u * a.k.mb + page0 + i];
-      if (blk < 0 || blk >= a.k.npb) {
-        raise_flag(a.flags, kFlagBlock);
-        blk = 0;  // any in-pool block: the scores of this page are unspecified
-      }
-      s_bt[i] = blk;
-    }
+    const int npcap = (min(tile0 + a.tile, a.n_max) - 1) / a.k.bs - page0 + 1;  // tile0 < n_max
+    for (int i = threadIdx.x; i < npcap; i += 256) s_bt[i] = a.k.bt[(int64_t)u * a.k.mb + page0 + i];
     __syncthreads();
   }
 
-  // ---- B operands of this lane's column
-  int head = -1;
-  bool lo = false;
-  if (col < G) head = col;
-  else if (col >= 8 && col < 8 + G) { head = col - 8; lo = true; }
+  // ---- B operands of this lane's column, in the order k_coef wrote them
   bf16x8 bdot[S::NKC], bna[S::NNC], bnb[S::NNC];
   {
-    const float* crow = a.C + ((size_t)u * hq + g * G + (head < 0 ? 0 : head)) * D;
-    const float* nrow = a.N + ((size_t)u * hq + g * G + (head < 0 ? 0 : head)) * S::F;
+    constexpr int NB = S::NKC + 2 * S::NNC;
+    const u32x4* bsrc = reinterpret_cast<const u32x4*>(a.B) + (size_t)ti.ug * NB * 64 + lane;
 #pragma unroll
-    for (int i = 0; i < S::NKC; ++i) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (head >= 0) {
-        const int e0 = chunk_elem<D>(i, grp);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t hi, lw;
-          split_bf16(crow[e0 + 2 * j], crow[e0 + 2 * j + 1], hi, lw);
-          w[j] = lo ? lw : hi;
-        }
-      }
-      bdot[i] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int i = 0; i < S::NKC; ++i) bdot[i] = __builtin_bit_cast(bf16x8, bsrc[i * 64]);
 #pragma unroll
     for (int i = 0; i < S::NNC; ++i) {
-      u32x4 wa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
-      if (head >= 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x0 = nrow[lane_band<D, P>(8 * i + 2 * j, grp)];
-          const float x1 = nrow[lane_band<D, P>(8 * i + 2 * j + 1, grp)];
-          uint32_t hi, lw;
-          split_bf16(x0, x1, hi, lw);
-          wa[j] = lo ? lw : hi;
-          wb[j] = lo ? 0u : hi;
-        }
-      }
-      bna[i] = __builtin_bit_cast(bf16x8, wa);
-      bnb[i] = __builtin_bit_cast(bf16x8, wb);
+      bna[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + i) * 64]);
+      bnb[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + S::NNC + i) * 64]);
+    }
+  }
+
+  // the first stage, unconditionally and before len[u] is known: a wave past n_max
+  // (in the last tile) reloads row kcap - 1 = n_max - 1 >= tile0, which exists
+  Stage<D> cA, cB;
+  load_stage<D, PAGED>(cA, a.k, u, g, kw0, kcap, col, grp, s_bt, page0);
+
+  tile_len(a, ti, n_loaded, true);
+  const int n = ti.n;
+  if (PAGED) {
+    const int last = min(tile0 + a.tile, n) - 1;
+    const int npages = last >= tile0 ? last / a.k.bs - page0 + 1 : 0;
+    for (int i = threadIdx.x; i < npages; i += 256) {
+      const int blk = s_bt[i];
+      if (blk < 0 || blk >= a.k.npb) raise_flag(a.flags, kFlagBlock);  // those scores are unspecified
     }
   }
 
   const bool owner = col >= 8 && col < 8 + G;  // lanes that hold a final score
   float* s_row = s_raw + (owner ? col - 8 : 0) * RS - tile0;
-  const int kw0 = tile0 + wave * kpw;
   const int kend = min(kw0 + kpw, n);   // this wave's keys: [kw0, kend)
 
   // scores of one loaded stage: dot-product MFMAs of every block first (independent
@@ -412,11 +465,11 @@ __device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float
     }
   };
 
-  // ---- two-stage register pipeline over the wave's keys [kw0, kend): the loads of
-  // the next stage are in flight while the current stage computes
+  // ---- register double buffer over the wave's keys [kw0, kend): the next stage's
+  // loads are issued while the current stage computes.  (Keeping two stages in
+  // flight across each wait measured slower on the full cache: more outstanding
+  // requests per wave did not raise the delivered bandwidth.)
   if (kw0 < kend) {
-    Stage<D> cA, cB;
-    load_stage<D, PAGED>(cA, a.k, u, g, kw0, kend, col, grp, s_bt, page0);
     for (int kb = kw0;; kb += 2 * STAGE) {
       load_stage<D, PAGED>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
       compute(cA, kb);
@@ -450,19 +503,33 @@ __device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float
   // run on other CUs and XCDs.
   const int c0 = max(a.sink, tile0) - tile0;
   const int c1 = min(n - a.window, tile0 + tlen) - tile0;
+  // lane l reads 16-byte groups 4 (l + 64 k): all of a pass's LDS loads are
+  // independent and in flight together
+  const int ngrp = (a.tile / 4 + 63) / 64;     // 16-byte groups per lane
   for (int h = wave; h < G; h += 4) {
     const float* src = s_raw + h * RS;
     float acc = 0.0f;
-    for (int i = c0 + lane; i < c1; i += 64) acc += src[i];
+    for (int k = 0; k < ngrp; ++k) {
+      const int i = 4 * (lane + 64 * k);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (i + t >= c0 && i + t < c1) acc += x[t];
+    }
     double sum = (double)acc;
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
     const int cnt = max(0, c1 - c0);
     const double mean = cnt > 0 ? sum / cnt : 0.0;
     const float mf = (float)mean;
     float q = 0.0f;
-    for (int i = c0 + lane; i < c1; i += 64) {
-      const float dv = src[i] - mf;
-      q = __builtin_fmaf(dv, dv, q);
+    for (int k = 0; k < ngrp; ++k) {
+      const int i = 4 * (lane + 64 * k);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float dv = x[t] - mf;
+        if (i + t >= c0 && i + t < c1) q = __builtin_fmaf(dv, dv, q);
+      }
     }
     double m2 = (double)q;
     for (int o = 32; o > 0; o >>= 1) m2 += __shfl_xor(m2, o);
@@ -480,13 +547,8 @@ __device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // every publishing store is complete before the arrival below is counted: the
-  // stores and the counter are agent-scope atomics, coherent across XCDs by
-  // themselves, so only their order needs enforcing (an agent-scope release fence
-  // would also write back this XCD's whole L2, once per tile)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.arrive + ti.ug, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // nothing waits for these stores: each moment is a single-copy-atomic 8-byte
+  // store, and a reader takes it as published once it no longer reads kUnpublished
 }
 
 // Waits until every tile of the (unit, KV head) of `ti` has published its moments,
@@ -494,36 +556,40 @@ __device__ inline void score_phase(const ScoreArgs& a, const TileInfo& ti, float
 // GQA group onto the KV head [Fold note, sec. 4: normalize-then-max; mean is the
 // other variant] and writes the aggregate; protected slots (sinks, recent window)
 // get +inf.
-__device__ inline void finalize_tile(const ScoreArgs& a, const TileInfo& ti, const float* s_raw, uint32_t* s_hist) {
+__device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, const float* s_raw, uint32_t* s_hist) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = a.group;
   const int hq = a.hkv * G;
   const int RS = a.tile + 16;
   __shared__ float s_mean[kMaxGroup], s_inv[kMaxGroup];
-  if (threadIdx.x == 0) {
-    const int32_t* ctr = a.arrive + ti.ug;
-    int spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_tiles) {
-      __builtin_amdgcn_s_sleep(8);
-      if (++spins >= kSpinLimit) {
-        raise_flag(a.flags, kFlagSync);
-        break;
-      }
-    }
-  }
-  __syncthreads();
+  tile_len(a, ti, a.len[ti.u], false);
 
-  // the group's mean and standard deviation per query head (fixed summation order:
-  // lane j takes tiles j, j + 64, ...; then a fixed shuffle tree)
+  // the group's mean and standard deviation per query head, from every tile's
+  // moments (fixed summation order: lane j takes tiles j, j + 64, ...; then a fixed
+  // shuffle tree); a wave polls until none of its head's moments reads kUnpublished
   for (int h = wave; h < G; h += 4) {
     const unsigned long long* p =
         reinterpret_cast<const unsigned long long*>(a.part + ((size_t)ti.u * hq + ti.g * G + h) * a.n_tiles * 3);
-    double c = 0.0, s1 = 0.0, s2 = 0.0;
-    for (int j = lane; j < a.n_tiles; j += 64) {
-      c += __longlong_as_double(__hip_atomic_load(p + 3 * j + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      s1 += __longlong_as_double(__hip_atomic_load(p + 3 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      s2 += __longlong_as_double(__hip_atomic_load(p + 3 * j + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    double c, s1, s2;
+    for (int polls = 0;; ++polls) {
+      c = s1 = s2 = 0.0;
+      bool missing = false;
+      for (int j = lane; j < a.n_tiles; j += 64) {
+        const unsigned long long x0 = __hip_atomic_load(p + 3 * j + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long x1 = __hip_atomic_load(p + 3 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long x2 = __hip_atomic_load(p + 3 * j + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        missing |= (x0 == kUnpublished) | (x1 == kUnpublished) | (x2 == kUnpublished);
+        c += __longlong_as_double(x0);
+        s1 += __longlong_as_double(x1);
+        s2 += __longlong_as_double(x2);
+      }
+      if (__ballot(missing) == 0) break;
+      if (polls >= kPollLimit) {
+        if (lane == 0) raise_flag(a.flags, kFlagSync);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
     }
     for (int o = 32; o > 0; o >>= 1) {
       c += __shfl_xor(c, o);
@@ -606,9 +672,9 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
     __syncthreads();
     const int t = s_t;
     __syncthreads();
-    if (t < total) score_phase<D, P, PAGED>(a, tile_info(a, t, true), b ? buf1 : buf0, s_bt);
+    if (t < total) score_phase<D, P, PAGED>(a, tile_info(a, t), b ? buf1 : buf0, s_bt);
     // s_bt served the current tile's score phase; finalize reuses it as histogram scratch
-    if (prev >= 0) finalize_tile(a, tile_info(a, prev, false), b ? buf0 : buf1, reinterpret_cast<uint32_t*>(s_bt));
+    if (prev >= 0) finalize_tile(a, tile_info(a, prev), b ? buf0 : buf1, reinterpret_cast<uint32_t*>(s_bt));
     if (t >= total) break;
     prev = t;
     b = !b;
@@ -966,9 +1032,20 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 // ============================================================================ launches
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   if (a.n_units == 0) return hipSuccess;
-  const unsigned chunks = (unsigned)((a.hq * (a.d / 2) + 255) / 256);
-  hipLaunchKernelGGL(k_coef, dim3(a.n_units, chunks), dim3(256), 0, s, a, offs);
-  return hipGetLastError();
+  const dim3 grid((unsigned)a.n_units, (unsigned)a.hkv);
+#define TRIA_COEF_CASE(DD, PP)                                                   \
+  if (a.d == DD && a.pairing == PP) {                                           \
+    hipLaunchKernelGGL((k_coef<DD, PP>), grid, dim3(256), 0, s, a, offs);       \
+    return hipGetLastError();                                                   \
+  }
+  TRIA_COEF_CASE(64, 0)
+  TRIA_COEF_CASE(64, 1)
+  TRIA_COEF_CASE(128, 0)
+  TRIA_COEF_CASE(128, 1)
+  TRIA_COEF_CASE(256, 0)
+  TRIA_COEF_CASE(256, 1)
+#undef TRIA_COEF_CASE
+  return hipErrorInvalidValue;
 }
 
 size_t score_lds(int group, bool paged) {
