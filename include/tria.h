@@ -107,9 +107,10 @@ typedef struct tria_params {
  *   paged : base + (bt[u*max_blocks + i/block_size]*block_size + i%block_size)
  *                  * stride_slot + g*stride_head
  * (strides in bf16 elements, each a multiple of 8; base 16-byte aligned).
- * tria_score may read (and ignore) rows of slots in [len[u], n_max): a dense view
- * must be readable for every slot below n_max, and a paged view's table must
- * cover n_max slots (its ids past len[u] may be anything, -1 included).  */
+ * tria_score and tria_compact may read (and ignore) rows of slots in
+ * [len[u], n_max): a dense source view must be readable for every slot below
+ * n_max, and a paged view's table must cover n_max slots (its ids past len[u] may
+ * be anything, -1 included).  */
 typedef struct tria_kv_view {
   void* base;                 /* [device] bf16 rows                             */
   int64_t stride_unit;        /* dense only                                     */
@@ -212,6 +213,15 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
                          int32_t b_max, const int32_t* len, const int32_t* idx, const int32_t* cnt,
                          const tria_kv_view* k_dst, const tria_kv_view* v_dst, int32_t* pos_dst,
                          void* stream);
+
+/* Caps the number of workgroups tria_score's persistent kernel launches (0, the
+ * default, means as many as the device holds at once), for callers that keep
+ * compute units free for work on other streams.  A cap below the score tiles of
+ * one (unit, KV head) (n_max / 2048, or n_max / 1024 when group > 4, rounded up)
+ * makes tria_score return TRIA_ESHAPE.  Results do not depend on the cap: every
+ * tile's arithmetic and every reduction run in a fixed order.  Process-wide;
+ * returns the previous cap. */
+int32_t tria_score_max_workgroups(int32_t cap);
 
 /* Reads (after synchronising `stream`) and clears the device flag word of a
  * workspace.  Returns TRIA_OK and the OR of TRIA_FLAG_* in *flags. */

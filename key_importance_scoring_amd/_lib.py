@@ -21,7 +21,8 @@ AGG_MEAN, AGG_MAX = 0, 1
 FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
-           "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name")
+           "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name",
+           "tria_score_max_workgroups")
 
 
 class TriaError(RuntimeError):
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
     lib.tria_timing_read.argtypes = [POINTER(c_double), POINTER(c_int64), c_int32]
     lib.tria_kernel_name.restype = c_char_p
     lib.tria_kernel_name.argtypes = [c_int32]
+    lib.tria_score_max_workgroups.restype = c_int32
+    lib.tria_score_max_workgroups.argtypes = [c_int32]
     _lib = lib
     return lib
 
@@ -155,6 +158,11 @@ def tria_device_flags(ws, stream=None) -> int:
     out = c_int32(0)
     _check(load().tria_device_flags(ptr(ws), ctypes.byref(out), stream_handle(stream)))
     return int(out.value)
+
+
+def tria_score_max_workgroups(cap: int) -> int:
+    """Caps tria_score's persistent grid (0: device capacity); returns the previous cap."""
+    return int(load().tria_score_max_workgroups(int(cap)))
 
 
 def tria_timing_enable(on: bool) -> int:

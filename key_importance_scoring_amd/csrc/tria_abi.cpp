@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -65,6 +66,9 @@ tria_status launch_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return TRIA_OK;
   return fail(TRIA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
 }
+
+// cap on tria_score's persistent grid (0: the device's resident capacity)
+std::atomic<int32_t> g_score_wg_cap{0};
 
 // ------------------------------------------------------------------ validation
 tria_status check_params(const tria_params* p) {
@@ -201,6 +205,10 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   if (L.n_tiles > cap)
     return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the device holds %d",
                 n_max, L.n_tiles, cap);
+  const int wg_cap = g_score_wg_cap.load();
+  if (wg_cap > 0 && L.n_tiles > wg_cap)
+    return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the workgroup cap is %d",
+                n_max, L.n_tiles, wg_cap);
 
   char* w = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -223,7 +231,7 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
                      tria::score_tile_keys(p->group), L.n_tiles, p->agg,
                      len, B, raw, part, agg, next_tile, hist, flags};
-  e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, s); });
+  e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, wg_cap, s); });
   return launch_status(e, "k_score");
 }
 
@@ -270,7 +278,8 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
   if (!len || !idx || !cnt) return fail(TRIA_EINVAL, "a required device pointer is NULL");
   if (pos_src && pos_heads != 1 && pos_heads != p->n_kv_heads)
     return fail(TRIA_ESHAPE, "pos_heads %d must be 1 or n_kv_heads", pos_heads);
-  if (n_units == 0 || b_max == 0) return TRIA_OK;
+  // with no source slots no index is valid: nothing to copy
+  if (n_units == 0 || b_max == 0 || n_max == 0) return TRIA_OK;
 
   // out of place only: dense destinations must not overlap any source
   const int hkv = p->n_kv_heads, d = p->head_dim;
@@ -336,6 +345,10 @@ const char* tria_strerror(tria_status s) {
 }
 
 const char* tria_last_error(void) { return g_err; }
+
+int32_t tria_score_max_workgroups(int32_t cap) {
+  return g_score_wg_cap.exchange(cap < 0 ? 0 : cap);
+}
 
 int32_t tria_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_tmu);

@@ -125,7 +125,7 @@ struct CompactArgs {
 constexpr int kCompactRows = 64;   // kept rows per compaction workgroup
 
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
-hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s);
 // Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
 // of one (unit, KV head) must be resident together for the moment exchange.
 int score_capacity(int d, int pairing, bool paged, int group);

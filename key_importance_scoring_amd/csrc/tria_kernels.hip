@@ -1029,6 +1029,98 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 
 }  // namespace
 
+// Fast compaction for the common layouts: K and V sources both dense, or both paged
+// through one block table (likewise the destinations).  A thread copies 16 bytes of R rows; all of a step's loads
+// are issued before any is used, so a workgroup's 64 rows take one round trip for
+// the indices (and destination block ids), one for the source block ids and
+// positions (paged sources), and one for the rows.  Every load is unconditional:
+// rows past the count and invalid slots or block ids read a clamped, existing
+// address and are not stored.
+template <int D, bool SP, bool DP>
+__global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a) {
+  constexpr int LPR = D / 8;                // lanes per row, 16 bytes each
+  constexpr int RPP = 256 / LPR;            // rows per pass
+  constexpr int R = kCompactRows / RPP;     // rows per thread
+  const int rt = blockIdx.x % a.n_rtiles;
+  const int ug = blockIdx.x / a.n_rtiles;
+  const int u = ug / a.hkv, g = ug % a.hkv;
+  int K = a.cnt[u];
+  K = K < 0 ? 0 : (K > a.b_max ? a.b_max : K);
+  int n = a.len[u];
+  n = n < 0 ? 0 : (n > a.n_max ? a.n_max : n);
+  const int j0 = rt * kCompactRows;
+  if (j0 >= K) return;
+  const int part = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  const int32_t* ix = a.idx + (size_t)ug * a.b_max;
+  const int ph = a.pos_heads > 1 ? g : 0;
+  // without positions the (ignored) position loads read idx[0] of this row
+  const int32_t* psrc = a.pos_src ? a.pos_src + ((size_t)u * a.pos_heads + ph) * a.n_max : ix;
+  const int pmask = a.pos_src ? -1 : 0;
+
+  // step 1: kept slots and destination block ids
+  int slot[R], dblk[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int j = min(j0 + r0 + k * RPP, K - 1);
+    slot[k] = ix[j];
+    if (DP) dblk[k] = a.kd.bt[(int64_t)u * a.kd.mb + j / a.kd.bs];
+  }
+  // step 2: validity, source block ids, positions
+  bool ok[R];
+  int sblk[R], pos[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const bool in = j0 + r0 + k * RPP < K;
+    const bool valid = slot[k] >= 0 && slot[k] < n;
+    if (in && !valid && part == 0) raise_flag(a.flags, kFlagIndex);
+    ok[k] = in && valid;
+    slot[k] = valid ? slot[k] : 0;
+    if (SP) sblk[k] = a.ks.bt[(int64_t)u * a.ks.mb + slot[k] / a.ks.bs];
+    pos[k] = psrc[slot[k] & pmask];
+  }
+  // step 3: the rows
+  u32x4 kv[R], vv[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    int64_t ko, vo;
+    if (SP) {
+      const bool bad = sblk[k] < 0 || sblk[k] >= a.ks.npb;
+      if (ok[k] && bad && part == 0) raise_flag(a.flags, kFlagBlock);
+      ok[k] = ok[k] && !bad;
+      const int64_t b = bad ? 0 : sblk[k];
+      ko = (b * a.ks.bs + slot[k] % a.ks.bs) * a.ks.ss + (int64_t)g * a.ks.sh;
+      vo = (b * a.vs.bs + slot[k] % a.vs.bs) * a.vs.ss + (int64_t)g * a.vs.sh;
+    } else {
+      ko = (int64_t)u * a.ks.su + (int64_t)g * a.ks.sh + (int64_t)slot[k] * a.ks.ss;
+      vo = (int64_t)u * a.vs.su + (int64_t)g * a.vs.sh + (int64_t)slot[k] * a.vs.ss;
+    }
+    kv[k] = reinterpret_cast<const u32x4*>(a.ks.base + ko)[part];
+    vv[k] = reinterpret_cast<const u32x4*>(a.vs.base + vo)[part];
+  }
+  // step 4: stores
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int j = j0 + r0 + k * RPP;
+    int64_t ko, vo;
+    bool okd = ok[k];
+    if (DP) {
+      const bool bad = dblk[k] < 0 || dblk[k] >= a.kd.npb;
+      if (okd && bad && part == 0) raise_flag(a.flags, kFlagBlock);
+      okd = okd && !bad;
+      ko = ((int64_t)dblk[k] * a.kd.bs + j % a.kd.bs) * a.kd.ss + (int64_t)g * a.kd.sh;
+      vo = ((int64_t)dblk[k] * a.vd.bs + j % a.vd.bs) * a.vd.ss + (int64_t)g * a.vd.sh;
+    } else {
+      ko = (int64_t)u * a.kd.su + (int64_t)g * a.kd.sh + (int64_t)j * a.kd.ss;
+      vo = (int64_t)u * a.vd.su + (int64_t)g * a.vd.sh + (int64_t)j * a.vd.ss;
+    }
+    if (okd) {
+      reinterpret_cast<u32x4*>(a.kd.base + ko)[part] = kv[k];
+      reinterpret_cast<u32x4*>(a.vd.base + vo)[part] = vv[k];
+      if (part == 0 && a.pos_src && a.pos_dst) a.pos_dst[(size_t)ug * a.b_max + j] = pos[k];
+    }
+  }
+}
+
 // ============================================================================ launches
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   if (a.n_units == 0) return hipSuccess;
@@ -1082,11 +1174,12 @@ int score_capacity(int d, int pairing, bool paged, int group) {
   return per_cu * cus;
 }
 
-hipError_t launch_score(const ScoreArgs& a, int d, int pairing, hipStream_t s) {
+hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s) {
   const long tiles = (long)a.n_units * a.hkv * a.n_tiles;
   if (tiles == 0) return hipSuccess;
   const bool paged = a.k.bt != nullptr;
-  const int cap = score_capacity(d, pairing, paged, a.group);
+  int cap = score_capacity(d, pairing, paged, a.group);
+  if (max_wg > 0 && max_wg < cap) cap = max_wg;
   if (cap < a.n_tiles) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
   const size_t lds = score_lds(a.group, paged);
@@ -1129,6 +1222,31 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const long blocks = (long)a.n_units * a.hkv * a.n_rtiles;
   if (blocks == 0) return hipSuccess;
+  const bool sp = a.ks.bt != nullptr, dp = a.kd.bt != nullptr;
+  auto same_table = [](const auto& x, const auto& y) {
+    return x.bt == y.bt && (x.bt == nullptr || (x.bs == y.bs && x.mb == y.mb && x.npb == y.npb));
+  };
+  if (same_table(a.ks, a.vs) && same_table(a.kd, a.vd)) {
+#define TRIA_COMPACT_CASE(DD, SP, DP)                                                  \
+    if (a.d == DD && sp == SP && dp == DP) {                                           \
+      hipLaunchKernelGGL((k_compact_fast<DD, SP, DP>), dim3((unsigned)blocks), dim3(256), 0, s, a); \
+      return hipGetLastError();                                                        \
+    }
+    TRIA_COMPACT_CASE(64, false, false)
+    TRIA_COMPACT_CASE(64, false, true)
+    TRIA_COMPACT_CASE(64, true, false)
+    TRIA_COMPACT_CASE(64, true, true)
+    TRIA_COMPACT_CASE(128, false, false)
+    TRIA_COMPACT_CASE(128, false, true)
+    TRIA_COMPACT_CASE(128, true, false)
+    TRIA_COMPACT_CASE(128, true, true)
+    TRIA_COMPACT_CASE(256, false, false)
+    TRIA_COMPACT_CASE(256, false, true)
+    TRIA_COMPACT_CASE(256, true, false)
+    TRIA_COMPACT_CASE(256, true, true)
+#undef TRIA_COMPACT_CASE
+  }
+  // K and V in different layouts: one row at a time
   hipLaunchKernelGGL(k_compact, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -192,3 +192,13 @@ def test_last_error_names_the_problem():
         _score(n_max=4100)
     except kis.TriaError as e:
         assert "multiple of 16" in str(e)
+
+
+def test_score_workgroup_cap_is_process_wide_and_returns_previous():
+    prev = L.tria_score_max_workgroups(37)
+    try:
+        assert L.tria_score_max_workgroups(5) == 37
+        assert L.tria_score_max_workgroups(-4) == 5     # negative means no cap
+        assert L.tria_score_max_workgroups(0) == 0
+    finally:
+        L.tria_score_max_workgroups(prev)

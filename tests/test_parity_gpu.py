@@ -197,3 +197,67 @@ def test_full_size_sampled_units(name, keep_raw):
             assert np.isin(prot, blk[g]).all()
         assert (idx[unit, :, k:] == -1).all()
     _check_oracle_compaction(prob, kept)
+
+
+# ----------------------------------------------------------------------------- schedule
+
+SCHED = {
+    "sched_dense": C["qwen3_8b"].replace(name="sched_dense", n_layers=4),
+    "sched_g8": C["qwen3_32b"].replace(name="sched_g8", n_layers=2, n_kv=20000, budget=3000),
+    "sched_paged": C["batched_decode"].replace(name="sched_paged", n_seqs=8),
+}
+
+
+@pytest.mark.parametrize("name", list(SCHED))
+def test_score_schedule_independence(name):
+    """The score kernel's results do not depend on its persistent grid.  With the grid
+    capped at the tiles of one (unit, KV head), each workgroup claims many tiles, often
+    several of one (unit, KV head), and waits on far fewer peers than with the default
+    grid.  Aggregates, kept slots and compacted rows must be bit-identical."""
+    cfg = SCHED[name]
+    prob = _run(cfg)
+    assert prob.flags() == 0
+    n_tiles = -(-prob.n_max // (2048 if cfg.group <= 4 else 1024))
+    ref = [t.clone() for t in (prob.agg, prob.idx, prob.cnt, prob.K_out, prob.V_out, prob.pos_out)]
+    prev = L.tria_score_max_workgroups(0)
+    try:
+        for cap in (n_tiles, n_tiles + 3, 4 * n_tiles + 1):
+            L.tria_score_max_workgroups(cap)
+            for t in (prob.agg, prob.idx, prob.cnt, prob.K_out, prob.V_out, prob.pos_out):
+                t.zero_()
+            prob.run()
+            torch.cuda.synchronize()
+            assert prob.flags() == 0, cap
+            u = synth.units(cfg)
+            for unit in range(cfg.n_units):
+                n = int(u.lengths[unit])
+                assert torch.equal(prob.agg[unit, :, :n], ref[0][unit, :, :n]), (cap, unit)
+            for got, want in zip((prob.idx, prob.cnt, prob.K_out, prob.V_out, prob.pos_out), ref[1:]):
+                assert torch.equal(got, want), cap
+        # a cap below one (unit, KV head)'s tiles is rejected before any launch
+        L.tria_score_max_workgroups(n_tiles - 1)
+        with pytest.raises(L.TriaError) as err:
+            prob.score()
+        assert err.value.status == L.TRIA_ESHAPE
+    finally:
+        L.tria_score_max_workgroups(prev)
+
+
+def test_compaction_layout_paths_agree():
+    """K and V through one block table take the batched compaction kernel; V through
+    its own copy of the table takes the row-at-a-time kernel.  Both must copy the
+    same bits."""
+    cfg = C["batched_decode"].replace(name="compact_paths", n_seqs=3, n_kv=5000, ragged_min=1000)
+    prob = _run(cfg)
+    ref = [t.clone() for t in (prob.K_out, prob.V_out, prob.pos_out)]
+    for t in (prob.K_out, prob.V_out, prob.pos_out):
+        t.zero_()
+    d, hkv, bs = cfg.head_dim, cfg.n_kv_heads, cfg.block_size
+    bt2, dbt2 = prob.bt.clone(), prob.dbt.clone()
+    v_view = L.make_view(prob.V, 0, d, hkv * d, bt2, bs, bt2.shape[1], prob.paging.n_blocks)
+    vd_view = L.make_view(prob.V_out, 0, d, hkv * d, dbt2, bs, dbt2.shape[1], prob.paging.n_dst_blocks)
+    L.tria_compact(prob.params, prob.k_view, v_view, prob.pos, 1, cfg.n_units, prob.n_max, prob.b_max, prob.len,
+                   prob.idx, prob.cnt, prob.kd_view, vd_view, prob.pos_out, None)
+    torch.cuda.synchronize()
+    for got, want in zip((prob.K_out, prob.V_out, prob.pos_out), ref):
+        assert torch.equal(got, want)
