@@ -40,7 +40,9 @@ bool g_timing = false;
 std::vector<Rec> g_recs;
 
 // Runs `launch` on `stream`, bracketed by HIP events on the same stream when
-// timing is on.
+// timing is on.  The events skip the system-scope fence (an L2 writeback and
+// invalidate) a default event performs on record; each recorded event still idles
+// the GPU for several microseconds between kernels.
 template <class Fn>
 hipError_t timed(int id, hipStream_t stream, Fn&& launch) {
   bool on;
@@ -50,9 +52,9 @@ hipError_t timed(int id, hipStream_t stream, Fn&& launch) {
   }
   if (!on) return launch();
   Rec r{id, nullptr, nullptr};
-  hipError_t e = hipEventCreate(&r.a);
+  hipError_t e = hipEventCreateWithFlags(&r.a, hipEventDisableSystemFence);
   if (e != hipSuccess) return e;
-  e = hipEventCreate(&r.b);
+  e = hipEventCreateWithFlags(&r.b, hipEventDisableSystemFence);
   if (e != hipSuccess) return e;
   if ((e = hipEventRecord(r.a, stream)) != hipSuccess) return e;
   if ((e = launch()) != hipSuccess) return e;
@@ -164,7 +166,7 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   L.st = off;
   off += al256(ug * sizeof(tria::SelState));
   L.tiles = off;
-  off += al256(ug * (size_t)L.n_st * 4 * 3);
+  off += al256(ug * (size_t)L.n_st * 4 * 4);  // above-b1 counts, offsets, tie shares, candidates
   L.list = off;
   off += al256(ug * (size_t)n_max * 4);
   L.total = off;
@@ -258,7 +260,8 @@ tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, in
   const size_t nt = (size_t)n_units * p->n_kv_heads * L.n_st;
   tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, L.n_st, len, budget, agg,
                       reinterpret_cast<const uint32_t*>(w + L.hist), reinterpret_cast<tria::SelState*>(w + L.st),
-                      tiles, tiles + nt, tiles + 2 * nt, reinterpret_cast<int32_t*>(w + L.list), idx, cnt,
+                      tiles, tiles + nt, tiles + 2 * nt, tiles + 3 * nt, reinterpret_cast<int32_t*>(w + L.list), idx,
+                      cnt,
                       reinterpret_cast<int32_t*>(w)};
   hipError_t e = timed(kIdSelect, s, [&] { return tria::launch_select(sa, s); });
   return launch_status(e, "k_select");

@@ -84,7 +84,7 @@ struct SelState {
   int32_t krem;  // slots still to take from bin b1
   int32_t K;     // slots kept
   int32_t n;     // cached slots
-  int32_t m;     // candidates (slots of bin b1) listed
+  int32_t m;     // candidates (slots of bin b1)
   int32_t T;     // threshold order key
   int32_t keq;   // slots equal to T that are kept
   int32_t pad;
@@ -103,7 +103,8 @@ struct SelectArgs {
   int32_t* tile_gt;           // [U][Hkv][n_st] slots above b1 per tile
   int32_t* tile_off;          // [U][Hkv][n_st] output offset per tile
   int32_t* tile_eqb;          // [U][Hkv][n_st] tied slots kept per tile
-  int32_t* list;              // [U][Hkv][n_max] candidate slots (bin b1)
+  int32_t* tile_m;            // [U][Hkv][n_st] candidates (slots of bin b1) per tile
+  int32_t* list;              // [U][Hkv][n_max] candidate slots, tile j's from j * kSelTile
   int32_t* idx;               // [U][Hkv][b_max]
   int32_t* cnt;               // [U]
   int32_t* flags;

@@ -690,8 +690,8 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
 //                 k_score, gives the bin b1 holding the K-th largest; the binning is
 //                 monotone, so every slot in a higher bin is kept and every slot in a
 //                 lower bin dropped;
-//   k_sel_collect (per tile)  counts the tile's slots above b1 and appends the slots
-//                 of b1 to the group's candidate list;
+//   k_sel_collect (per tile)  counts the tile's slots above b1 and lists its slots of
+//                 b1 in the tile's own segment of the group's candidate list;
 //   k_sel_refine  (per group) exact radix passes (11 + 11 + 10 bits of the
 //                 order-preserving key) over the candidates give the threshold key T
 //                 and how many slots equal to T are kept (the lowest ones); then each
@@ -749,56 +749,62 @@ __device__ inline void find_digit(const uint32_t* hist, int nb, uint32_t krem, u
   __syncthreads();
 }
 
+// The selection's bounds for group ug: n cached slots, K kept, and the bin b1
+// holding the K-th largest aggregate (-1: keep everything; kBins: keep nothing) with
+// krem slots still to take from it; flags and cnt[u] are written here.
 __global__ __launch_bounds__(256) void k_sel_thresh(SelectArgs a) {
+  constexpr int NT = 256;
   const int ug = blockIdx.x;
-  const int u = ug / a.hkv;
-  const int g = ug % a.hkv;
-  const int tid = threadIdx.x;
-  const int n = clamp_len(a.len, u, a.n_max, g == 0 ? a.flags : nullptr);
-  int B = a.budget[u];
-  const int prot = min(n, a.sink + a.window);
-  if (B < 0 || (n > B && B < prot)) {
-    if (g == 0 && tid == 0) raise_flag(a.flags, kFlagBudget);
-    B = B < 0 ? 0 : B;
-  }
-  int K = B < n ? B : n;
-  if (K > a.b_max) {
-    if (g == 0 && tid == 0) raise_flag(a.flags, kFlagBmax);
-    K = a.b_max;
-  }
-  if (g == 0 && tid == 0) a.cnt[u] = K;
+  const int u = ug / a.hkv, g = ug % a.hkv;
+  const bool lead = g == 0 && threadIdx.x == 0;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wtot[4];
   __shared__ uint32_t sh[2];
-  int b1;
-  uint32_t krem = 0;
-  if (K == 0) {
-    b1 = kBins;       // no bin is above it: nothing kept
-  } else if (K >= n) {
-    b1 = -1;          // every bin is above it: everything kept
+  struct {
+    int n, K, b1;
+    uint32_t krem;
+  } r;
+  r.n = clamp_len(a.len, u, a.n_max, lead ? a.flags : nullptr);
+  int B = a.budget[u];
+  const int prot = min(r.n, a.sink + a.window);
+  if (B < 0 || (r.n > B && B < prot)) {
+    if (lead) raise_flag(a.flags, kFlagBudget);
+    B = B < 0 ? 0 : B;
+  }
+  r.K = B < r.n ? B : r.n;
+  if (r.K > a.b_max) {
+    if (lead) raise_flag(a.flags, kFlagBmax);
+    r.K = a.b_max;
+  }
+  if (lead) a.cnt[u] = r.K;
+  r.krem = 0;
+  if (r.K == 0) {
+    r.b1 = kBins;
+  } else if (r.K >= r.n) {
+    r.b1 = -1;
   } else {
     const uint32_t* gh = a.hist + (size_t)ug * kBins;
-    for (int i = tid; i < kBins; i += 256) hist[i] = gh[i];
+    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = gh[i];
     __syncthreads();
     uint32_t d, above;
-    find_digit<256>(hist, kBins, (uint32_t)K, wtot, sh, d, above);
-    b1 = (int)d;
-    krem = (uint32_t)K - above;
+    find_digit<NT>(hist, kBins, (uint32_t)r.K, wtot, sh, d, above);
+    r.b1 = (int)d;
+    r.krem = (uint32_t)r.K - above;
   }
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     SelState& st = a.st[ug];
-    st.b1 = b1;
-    st.krem = (int32_t)krem;
-    st.K = K;
-    st.n = n;
+    st.b1 = r.b1;
+    st.krem = (int32_t)r.krem;
+    st.K = r.K;
+    st.n = r.n;
     st.m = 0;
     st.T = 0;
     st.keq = 0;
   }
 }
 
-// Loads the 8 slots [s0, s0 + 8) of a row (two 16-byte loads; s0 < n <= n_max and
-// n_max a multiple of 16, so the loads stay inside the row).
+// Loads the 8 slots [s0, s0 + 8) of a row (two 16-byte loads; s0 + 8 <= n_max, n_max a
+// multiple of 16, so the loads stay inside the row).
 __device__ inline void load8(const float* row, int s0, float (&x)[8]) {
   const f32x4 lo = *reinterpret_cast<const f32x4*>(row + s0);
   const f32x4 hi = *reinterpret_cast<const f32x4*>(row + s0 + 4);
@@ -812,58 +818,88 @@ __device__ inline void load8(const float* row, int s0, float (&x)[8]) {
 __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
   const int j = blockIdx.x % a.n_st;
-  const int u = ug / a.hkv;
   const int tid = threadIdx.x;
-  const SelState st = a.st[ug];
   __shared__ uint32_t wtot[4];
-  __shared__ uint32_t s_base;
+  // the tile's aggregates (clamped inside the row) and the group's bounds, together
   const int s0 = j * kSelTile + 8 * tid;
-  uint32_t cgt = 0, cm = 0;
   float x[8];
-  if (s0 < st.n) {
-    load8(a.agg + ((size_t)u * a.hkv + (ug % a.hkv)) * a.n_max, s0, x);
+  load8(a.agg + (size_t)ug * a.n_max, min(s0, a.n_max - 8), x);
+  const SelState bd = a.st[ug];
+  uint32_t cgt = 0, cm = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (s0 + k < st.n) {
-        const int bin = lin_bin(x[k]);
-        cgt += bin > st.b1 ? 1u : 0u;
-        cm += bin == st.b1 ? 1u : 0u;
-      }
+  for (int k = 0; k < 8; ++k) {
+    if (s0 + k < bd.n) {
+      const int bin = lin_bin(x[k]);
+      cgt += bin > bd.b1 ? 1u : 0u;
+      cm += bin == bd.b1 ? 1u : 0u;
     }
   }
   const uint32_t gt_tot = block_scan_incl<256>(cgt, wtot);
   const uint32_t m_incl = block_scan_incl<256>(cm, wtot);
   if (tid == 255) {
     a.tile_gt[blockIdx.x] = (int32_t)gt_tot;
-    s_base = m_incl ? (uint32_t)atomicAdd(&a.st[ug].m, (int32_t)m_incl) : 0u;
+    a.tile_m[blockIdx.x] = (int32_t)m_incl;
   }
-  __syncthreads();
+  // this tile's candidates, in slot order, at the start of its segment
+  // [j kSelTile, (j + 1) kSelTile) of the group's list
   if (cm) {
-    int32_t* list = a.list + (size_t)ug * a.n_max;
-    uint32_t pos = s_base + m_incl - cm;
+    int32_t* list = a.list + (size_t)ug * a.n_max + (size_t)j * kSelTile;
+    uint32_t pos = m_incl - cm;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (s0 + k < st.n && lin_bin(x[k]) == st.b1 && pos < (uint32_t)a.n_max) list[pos++] = s0 + k;
+      if (s0 + k < bd.n && lin_bin(x[k]) == bd.b1) list[pos++] = s0 + k;
   }
 }
 
 __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   const int ug = blockIdx.x;
-  const int u = ug / a.hkv;
   const int tid = threadIdx.x;
-  const SelState st = a.st[ug];
-  const float* row = a.agg + ((size_t)u * a.hkv + (ug % a.hkv)) * a.n_max;
+  const float* row = a.agg + (size_t)ug * a.n_max;
   const int32_t* list = a.list + (size_t)ug * a.n_max;
-  const int m = min(st.m, a.n_max);
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t wtot[8];
   __shared__ uint32_t sh[2];
   __shared__ int32_t s_gtb[kMaxSelTiles], s_eqc[kMaxSelTiles];
+  __shared__ int32_t s_pre[kMaxSelTiles + 1];   // candidates before each tile's segment
+
+  const SelState bd = a.st[ug];
+  // candidate i lives in tile seg(i)'s segment, at position i - s_pre[seg(i)]
+  {
+    const int per = (a.n_st + 511) / 512;   // consecutive tiles per thread
+    const int t0 = tid * per;
+    int32_t c[4] = {0, 0, 0, 0};            // per <= kMaxSelTiles / 512 = 4
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < per && t0 + i < a.n_st) {
+        c[i] = a.tile_m[(size_t)ug * a.n_st + t0 + i];
+        local += (uint32_t)c[i];
+      }
+    uint32_t run = block_scan_incl<512>(local, wtot) - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < per && t0 + i < a.n_st) {
+        s_pre[t0 + i] = (int32_t)run;
+        run += (uint32_t)c[i];
+      }
+    if (t0 < a.n_st && t0 + per >= a.n_st) s_pre[a.n_st] = (int32_t)run;   // the thread with the last tile
+    if (a.n_st == 0 && tid == 0) s_pre[0] = 0;
+  }
+  __syncthreads();
+  const int m = s_pre[a.n_st];
+  auto cand = [&](int i) {
+    int lo = 0, hi = a.n_st - 1;   // the last tile whose segment starts at or before i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return list[(size_t)lo * kSelTile + (i - s_pre[lo])];
+  };
 
   uint32_t T = 0, keq = 0;
-  const bool refine = st.b1 >= 0 && st.b1 < kBins;
+  const bool refine = bd.b1 >= 0 && bd.b1 < kBins;
   if (refine) {
-    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)st.krem;
+    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)bd.krem;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
       const int sft = pass == 0 ? 21 : (pass == 1 ? 10 : 0);   // digits of 11, 11, 10 bits
@@ -871,7 +907,7 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
       for (int i = tid; i < nb; i += 512) hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < m; i += 512) {
-        const uint32_t key = order_key(row[list[i]]);
+        const uint32_t key = order_key(row[cand(i)]);
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sft) & (nb - 1)], 1u);
       }
       __syncthreads();
@@ -892,7 +928,7 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   __syncthreads();
   if (refine) {
     for (int i = tid; i < m; i += 512) {
-      const int slot = list[i];
+      const int slot = cand(i);
       const uint32_t key = order_key(row[slot]);
       if (key > T) atomicAdd(&s_gtb[slot / kSelTile], 1);
       else if (key == T) atomicAdd(&s_eqc[slot / kSelTile], 1);
@@ -928,27 +964,29 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
     off += (uint32_t)a.tile_gt[(size_t)ug * a.n_st + jj] + (uint32_t)s_gtb[jj] + share;
   }
   if (tid == 0) {
+    a.st[ug].m = m;
     a.st[ug].T = (int32_t)T;
     a.st[ug].keq = (int32_t)keq;
   }
-  int32_t* out = a.idx + ((size_t)u * a.hkv + (ug % a.hkv)) * a.b_max;
-  for (int i = st.K + tid; i < a.b_max; i += 512) out[i] = -1;
+  int32_t* out = a.idx + (size_t)ug * a.b_max;
+  for (int i = bd.K + tid; i < a.b_max; i += 512) out[i] = -1;
 }
 
 __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
-  const int u = ug / a.hkv;
   const int tid = threadIdx.x;
-  const SelState st = a.st[ug];
-  const uint32_t T = (uint32_t)st.T;
-  const uint32_t eqb = (uint32_t)a.tile_eqb[blockIdx.x];
-  const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
   __shared__ uint32_t wtot[4];
+  // every load at once: the tile's aggregates (clamped inside the row), the group's
+  // state and the tile's offset and tie share
   const int s0 = (blockIdx.x % a.n_st) * kSelTile + 8 * tid;
   float x[8];
+  load8(a.agg + (size_t)ug * a.n_max, min(s0, a.n_max - 8), x);
+  const SelState st = a.st[ug];
+  const uint32_t eqb = (uint32_t)a.tile_eqb[blockIdx.x];
+  const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
+  const uint32_t T = (uint32_t)st.T;
   uint32_t gtm = 0, eqm = 0;   // per-slot bit masks
-  if (s0 < st.n) {
-    load8(a.agg + ((size_t)u * a.hkv + (ug % a.hkv)) * a.n_max, s0, x);
+  {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (s0 + k < st.n) {
@@ -975,7 +1013,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   }
   const uint32_t nk = (uint32_t)__popc(keep);
   uint32_t pos = off + block_scan_incl<256>(nk, wtot) - nk;
-  int32_t* out = a.idx + ((size_t)u * a.hkv + (ug % a.hkv)) * a.b_max;
+  int32_t* out = a.idx + (size_t)ug * a.b_max;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if ((keep >> k) & 1u) {
@@ -1211,11 +1249,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tiles) {
+    hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_sel_refine, dim3((unsigned)groups), dim3(512), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sel_emit, dim3(tiles), dim3(256), 0, s, a);
+  if (tiles) hipLaunchKernelGGL(k_sel_emit, dim3(tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
