@@ -223,6 +223,17 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
  * returns the previous cap. */
 int32_t tria_score_max_workgroups(int32_t cap);
 
+/* How tria_select distributes its work.  Both strategies keep the same slots
+ * (bit-identical idx and cnt).
+ *   TRIA_SELECT_AUTO      the faster one measured on MI355X: tiled (the default);
+ *   TRIA_SELECT_PER_GROUP one workgroup selects a whole (unit, KV head) from
+ *                         registers (falls back to tiled when n_max > 32768);
+ *   TRIA_SELECT_TILED     tiles of 2048 slots count and emit in parallel, with
+ *                         per-group threshold and refinement steps between.
+ * Process-wide; returns the previous strategy (an unknown value selects AUTO). */
+typedef enum { TRIA_SELECT_AUTO = 0, TRIA_SELECT_PER_GROUP = 1, TRIA_SELECT_TILED = 2 } tria_select_strategy_t;
+int32_t tria_select_strategy(int32_t strategy);
+
 /* Reads (after synchronising `stream`) and clears the device flag word of a
  * workspace.  Returns TRIA_OK and the OR of TRIA_FLAG_* in *flags. */
 tria_status tria_device_flags(void* ws, int32_t* flags, void* stream);

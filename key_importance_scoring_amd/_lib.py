@@ -22,7 +22,7 @@ FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC 
 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
            "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name",
-           "tria_score_max_workgroups")
+           "tria_score_max_workgroups", "tria_select_strategy")
 
 
 class TriaError(RuntimeError):
@@ -53,6 +53,12 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m key_importance_scoring_amd.build`")
+    # torch ships its own HIP runtime: loaded first, it is the one the library binds
+    # to; loaded after, a second runtime would not know torch's device memory
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     lib.tria_workspace_size.restype = c_size_t
     lib.tria_workspace_size.argtypes = [POINTER(TriaParams), c_int32, c_int32]
@@ -81,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.tria_kernel_name.argtypes = [c_int32]
     lib.tria_score_max_workgroups.restype = c_int32
     lib.tria_score_max_workgroups.argtypes = [c_int32]
+    lib.tria_select_strategy.restype = c_int32
+    lib.tria_select_strategy.argtypes = [c_int32]
     _lib = lib
     return lib
 
@@ -158,6 +166,14 @@ def tria_device_flags(ws, stream=None) -> int:
     out = c_int32(0)
     _check(load().tria_device_flags(ptr(ws), ctypes.byref(out), stream_handle(stream)))
     return int(out.value)
+
+
+SELECT_AUTO, SELECT_PER_GROUP, SELECT_TILED = range(3)
+
+
+def tria_select_strategy(strategy: int) -> int:
+    """Sets tria_select's work distribution (SELECT_*); returns the previous one."""
+    return int(load().tria_select_strategy(int(strategy)))
 
 
 def tria_score_max_workgroups(cap: int) -> int:

@@ -71,6 +71,8 @@ tria_status launch_status(hipError_t e, const char* what) {
 
 // cap on tria_score's persistent grid (0: the device's resident capacity)
 std::atomic<int32_t> g_score_wg_cap{0};
+// tria_select's work distribution (tria_select_strategy_t)
+std::atomic<int32_t> g_select_strategy{TRIA_SELECT_AUTO};
 
 // ------------------------------------------------------------------ validation
 tria_status check_params(const tria_params* p) {
@@ -263,7 +265,8 @@ tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, in
                       tiles, tiles + nt, tiles + 2 * nt, tiles + 3 * nt, reinterpret_cast<int32_t*>(w + L.list), idx,
                       cnt,
                       reinterpret_cast<int32_t*>(w)};
-  hipError_t e = timed(kIdSelect, s, [&] { return tria::launch_select(sa, s); });
+  const int strategy = g_select_strategy.load();
+  hipError_t e = timed(kIdSelect, s, [&] { return tria::launch_select(sa, strategy, s); });
   return launch_status(e, "k_select");
 }
 
@@ -348,6 +351,11 @@ const char* tria_strerror(tria_status s) {
 }
 
 const char* tria_last_error(void) { return g_err; }
+
+int32_t tria_select_strategy(int32_t strategy) {
+  if (strategy != TRIA_SELECT_PER_GROUP && strategy != TRIA_SELECT_TILED) strategy = TRIA_SELECT_AUTO;
+  return g_select_strategy.exchange(strategy);
+}
 
 int32_t tria_score_max_workgroups(int32_t cap) {
   return g_score_wg_cap.exchange(cap < 0 ? 0 : cap);

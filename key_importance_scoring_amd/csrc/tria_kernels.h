@@ -90,8 +90,12 @@ struct SelState {
   int32_t pad;
 };
 
-constexpr int kSelTile = 2048;          // slots per selection tile (8 per thread)
-constexpr int kMaxSelTiles = 2048;      // per (unit, KV head): n_max <= 4M
+#ifndef TRIA_SEL_TILE
+#define TRIA_SEL_TILE 2048
+#endif
+constexpr int kSelTile = TRIA_SEL_TILE; // slots per selection tile (kSelTile / 256 per thread)
+constexpr int kSelGroupMax = 32768;     // per-group selection: 512 threads x 64 slots in registers
+constexpr int kMaxSelTiles = 2048;      // per (unit, KV head): n_max <= 2048 kSelTile
 
 struct SelectArgs {
   int32_t n_units, n_max, b_max, hkv, sink, window, n_st;
@@ -130,7 +134,8 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
 // Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
 // of one (unit, KV head) must be resident together for the moment exchange.
 int score_capacity(int d, int pairing, bool paged, int group);
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// strategy: 0 automatic, 1 per group (when n_max fits), 2 tiled
+hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
 }  // namespace tria

@@ -803,15 +803,20 @@ __global__ __launch_bounds__(256) void k_sel_thresh(SelectArgs a) {
   }
 }
 
-// Loads the 8 slots [s0, s0 + 8) of a row (two 16-byte loads; s0 + 8 <= n_max, n_max a
-// multiple of 16, so the loads stay inside the row).
-__device__ inline void load8(const float* row, int s0, float (&x)[8]) {
-  const f32x4 lo = *reinterpret_cast<const f32x4*>(row + s0);
-  const f32x4 hi = *reinterpret_cast<const f32x4*>(row + s0 + 4);
+// A selection tile's slots per thread: thread t takes the kSelTile / 256 consecutive
+// slots from s0 = tile0 + t kSelTile / 256.
+constexpr int kSelSpt = kSelTile / 256;
+static_assert(kSelSpt % 4 == 0 && kSelSpt <= 32, "slots per thread: whole 16-byte loads, one 32-bit mask");
+
+// Loads the slots [s0, s0 + kSelSpt) of a row with 16-byte loads, each clamped inside
+// the row (n_max is a multiple of 16): values of slots at or past n_max are garbage
+// and never used.
+__device__ inline void load_slots(const float* row, int s0, int n_max, float (&x)[kSelSpt]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[k] = lo[k];
-    x[k + 4] = hi[k];
+  for (int i = 0; i < kSelSpt / 4; ++i) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + min(s0 + 4 * i, n_max - 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[4 * i + t] = v[t];
   }
 }
 
@@ -820,14 +825,14 @@ __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   const int j = blockIdx.x % a.n_st;
   const int tid = threadIdx.x;
   __shared__ uint32_t wtot[4];
-  // the tile's aggregates (clamped inside the row) and the group's bounds, together
-  const int s0 = j * kSelTile + 8 * tid;
-  float x[8];
-  load8(a.agg + (size_t)ug * a.n_max, min(s0, a.n_max - 8), x);
+  // the tile's aggregates and the group's bounds, together
+  const int s0 = j * kSelTile + kSelSpt * tid;
+  float x[kSelSpt];
+  load_slots(a.agg + (size_t)ug * a.n_max, s0, a.n_max, x);
   const SelState bd = a.st[ug];
   uint32_t cgt = 0, cm = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kSelSpt; ++k) {
     if (s0 + k < bd.n) {
       const int bin = lin_bin(x[k]);
       cgt += bin > bd.b1 ? 1u : 0u;
@@ -846,7 +851,7 @@ __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
     int32_t* list = a.list + (size_t)ug * a.n_max + (size_t)j * kSelTile;
     uint32_t pos = m_incl - cm;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < kSelSpt; ++k)
       if (s0 + k < bd.n && lin_bin(x[k]) == bd.b1) list[pos++] = s0 + k;
   }
 }
@@ -978,9 +983,9 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   __shared__ uint32_t wtot[4];
   // every load at once: the tile's aggregates (clamped inside the row), the group's
   // state and the tile's offset and tie share
-  const int s0 = (blockIdx.x % a.n_st) * kSelTile + 8 * tid;
-  float x[8];
-  load8(a.agg + (size_t)ug * a.n_max, min(s0, a.n_max - 8), x);
+  const int s0 = (blockIdx.x % a.n_st) * kSelTile + kSelSpt * tid;
+  float x[kSelSpt];
+  load_slots(a.agg + (size_t)ug * a.n_max, s0, a.n_max, x);
   const SelState st = a.st[ug];
   const uint32_t eqb = (uint32_t)a.tile_eqb[blockIdx.x];
   const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
@@ -988,7 +993,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   uint32_t gtm = 0, eqm = 0;   // per-slot bit masks
   {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < kSelSpt; ++k) {
       if (s0 + k < st.n) {
         const int bin = lin_bin(x[k]);
         const uint32_t key = order_key(x[k]);
@@ -1004,25 +1009,142 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   const uint32_t eq_before = block_scan_incl<256>(ne, wtot) - ne;
   uint32_t keep = gtm;
   uint32_t r = eq_before;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if ((eqm >> k) & 1u) {
-      if (r < eqb) keep |= 1u << k;
-      ++r;
-    }
+  for (uint32_t m = eqm; m; m &= m - 1) {
+    if (r < eqb) keep |= m & (~m + 1);
+    ++r;
   }
   const uint32_t nk = (uint32_t)__popc(keep);
   uint32_t pos = off + block_scan_incl<256>(nk, wtot) - nk;
   int32_t* out = a.idx + (size_t)ug * a.b_max;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    if ((keep >> k) & 1u) {
-      // positions are < K by construction; the bound keeps a miscount from ever
-      // writing past the caller's b_max row
-      if (pos < (uint32_t)st.K) out[pos] = s0 + k;
-      ++pos;
-    }
+  for (uint32_t m = keep; m; m &= m - 1) {
+    // positions are < K by construction; the bound keeps a miscount from ever
+    // writing past the caller's b_max row
+    if (pos < (uint32_t)st.K) out[pos] = s0 + __ffs(m) - 1;
+    ++pos;
   }
+}
+
+// ---------------------------------------------------------------------------- per group
+// The whole selection of one (unit, KV head) in one workgroup of 512 threads, for
+// rows of at most kSelGroupMax slots: thread t holds the aggregates of the 64
+// consecutive slots [64 t, 64 t + 64) in registers.  The histogram built by k_score
+// gives b1 and krem as in k_sel_thresh; three radix passes run straight over the
+// thread's values of bin b1 (no candidate list); then per-thread counts of kept and
+// tied slots, two block scans, and the thread writes its kept slots in order.  Ties
+// at the threshold key are kept lowest slot first, as in the tile-parallel kernels.
+// Makes the compiler treat the values as changed, so that keys and bins are formed
+// again in each pass instead of being kept in 64 more registers per thread.
+template <int N>
+__device__ inline void opaque(float (&x)[N]) {
+#pragma unroll
+  for (int v = 0; v < N; ++v) asm volatile("" : "+v"(x[v]));
+}
+
+__global__ __launch_bounds__(512) void k_sel_group(SelectArgs a) {
+  constexpr int NT = 512, VPT = 64;
+  const int ug = blockIdx.x;
+  const int u = ug / a.hkv, g = ug % a.hkv;
+  const int tid = threadIdx.x;
+  const bool lead = g == 0 && tid == 0;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wtot[NT / 64];
+  __shared__ uint32_t sh[2];
+
+  // the thread's values, loaded first (16-byte loads, clamped inside the row)
+  const float* row = a.agg + (size_t)ug * a.n_max;
+  const int s_lo = tid * VPT;
+  float x[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT / 4; ++i) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + min(s_lo + 4 * i, a.n_max - 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[4 * i + t] = v[t];
+  }
+
+  // bounds: n cached slots, K kept
+  const int n = clamp_len(a.len, u, a.n_max, lead ? a.flags : nullptr);
+  int B = a.budget[u];
+  const int prot = min(n, a.sink + a.window);
+  if (B < 0 || (n > B && B < prot)) {
+    if (lead) raise_flag(a.flags, kFlagBudget);
+    B = B < 0 ? 0 : B;
+  }
+  int K = B < n ? B : n;
+  if (K > a.b_max) {
+    if (lead) raise_flag(a.flags, kFlagBmax);
+    K = a.b_max;
+  }
+  if (lead) a.cnt[u] = K;
+
+  // the threshold: every slot of a bin above b1 is kept; in bin b1, keys above T and
+  // the lowest keq slots equal to T
+  int b1;
+  uint32_t T = 0, keq = 0;
+  if (K == 0) {
+    b1 = kBins;
+  } else if (K >= n) {
+    b1 = -1;
+  } else {
+    const uint32_t* gh = a.hist + (size_t)ug * kBins;
+    for (int i = tid; i < kBins; i += NT) hist[i] = gh[i];
+    __syncthreads();
+    uint32_t d, above;
+    find_digit<NT>(hist, kBins, (uint32_t)K, wtot, sh, d, above);
+    b1 = (int)d;
+    uint32_t krem = (uint32_t)K - above;
+    uint32_t prefix = 0, pmask = 0;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sft = pass == 0 ? 21 : (pass == 1 ? 10 : 0);   // digits of 11, 11, 10 bits
+      const int nb = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < nb; i += NT) hist[i] = 0;
+      __syncthreads();
+      opaque(x);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const uint32_t key = order_key(x[v]);
+        if (s_lo + v < n && lin_bin(x[v]) == b1 && (key & pmask) == prefix)
+          atomicAdd(&hist[(key >> sft) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t dd, ab;
+      find_digit<NT>(hist, nb, krem, wtot, sh, dd, ab);
+      prefix |= dd << sft;
+      pmask |= (uint32_t)(nb - 1) << sft;
+      krem -= ab;
+    }
+    T = prefix;
+    keq = krem;
+  }
+
+  // kept and tied slots of this thread (bit v: slot s_lo + v)
+  opaque(x);
+  uint64_t keep = 0, eq = 0;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int bin = lin_bin(x[v]);
+    const uint32_t key = order_key(x[v]);
+    const bool in = s_lo + v < n;
+    const bool gt = bin > b1 || (bin == b1 && key > T);
+    keep |= (uint64_t)(in && gt) << v;
+    eq |= (uint64_t)(in && bin == b1 && key == T) << v;
+  }
+  const uint32_t ne = (uint32_t)__popcll(eq);
+  uint32_t r = block_scan_incl<NT>(ne, wtot) - ne;   // tied slots in lower slots
+  for (uint64_t m = eq; m; m &= m - 1) {
+    if (r < keq) keep |= m & (~m + 1);
+    ++r;
+  }
+  const uint32_t nk = (uint32_t)__popcll(keep);
+  uint32_t pos = block_scan_incl<NT>(nk, wtot) - nk;
+  int32_t* out = a.idx + (size_t)ug * a.b_max;
+  for (uint64_t m = keep; m; m &= m - 1) {
+    // positions are < K by construction; the bound keeps a miscount from ever
+    // writing past the caller's b_max row
+    if (pos < (uint32_t)K) out[pos] = s_lo + __ffsll((unsigned long long)m) - 1;
+    ++pos;
+  }
+  for (int i = K + tid; i < a.b_max; i += NT) out[i] = -1;
 }
 
 // ============================================================================ k_compact
@@ -1242,9 +1364,17 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s) {
   const long groups = (long)a.n_units * a.hkv;
   if (groups == 0) return hipSuccess;
+  // one workgroup per group only on request: measured on MI355X it is 2x slower than
+  // the tile-parallel kernels (one 512-thread workgroup fills a CU, and its four
+  // threshold scans run back to back)
+  const bool fits = a.n_max <= kSelGroupMax;
+  if (fits && strategy == 1) {
+    hipLaunchKernelGGL(k_sel_group, dim3((unsigned)groups), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   const unsigned tiles = (unsigned)(groups * a.n_st);
   hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();

@@ -202,3 +202,13 @@ def test_score_workgroup_cap_is_process_wide_and_returns_previous():
         assert L.tria_score_max_workgroups(0) == 0
     finally:
         L.tria_score_max_workgroups(prev)
+
+
+def test_select_strategy_is_process_wide_and_returns_previous():
+    prev = L.tria_select_strategy(L.SELECT_TILED)
+    try:
+        assert L.tria_select_strategy(L.SELECT_PER_GROUP) == L.SELECT_TILED
+        assert L.tria_select_strategy(99) == L.SELECT_PER_GROUP     # unknown means automatic
+        assert L.tria_select_strategy(L.SELECT_AUTO) == L.SELECT_AUTO
+    finally:
+        L.tria_select_strategy(prev)

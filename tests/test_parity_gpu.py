@@ -92,6 +92,34 @@ def test_small_parity(name):
     _check_oracle_compaction(prob, kept)
 
 
+@pytest.fixture(params=[L.SELECT_TILED, L.SELECT_PER_GROUP], ids=["tiled", "per_group"])
+def strategy(request):
+    prev = L.tria_select_strategy(request.param)
+    yield request.param
+    L.tria_select_strategy(prev)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_select_strategies_agree(name):
+    """The per-group and tiled selections keep bit-identical slots (the small cases
+    have too few groups for the automatic choice to take the per-group kernel)."""
+    cfg = SMALL[name]
+    prev = L.tria_select_strategy(L.SELECT_TILED)
+    try:
+        prob = _run(cfg)
+        ref_idx, ref_cnt = prob.idx.clone(), prob.cnt.clone()
+        L.tria_select_strategy(L.SELECT_PER_GROUP)
+        prob.idx.fill_(-7)
+        prob.cnt.fill_(-7)
+        prob.select()
+        torch.cuda.synchronize()
+        assert prob.flags() == _expected_flags(cfg)
+        assert torch.equal(prob.cnt, ref_cnt)
+        assert torch.equal(prob.idx, ref_idx)
+    finally:
+        L.tria_select_strategy(prev)
+
+
 @pytest.mark.parametrize("name", ["q8_small", "lc_small", "bd_small"])
 def test_small_raw_against_direct_form(name):
     """The literal 17-offset average, not only the folded oracle."""
@@ -104,7 +132,7 @@ def test_small_raw_against_direct_form(name):
     check_raw(prob.raw[unit, g * cfg.group:(g + 1) * cfg.group, :n].cpu().numpy(), o_raw, f"{name} direct")
 
 
-def test_zero_statistics_break_ties_by_slot():
+def test_zero_statistics_break_ties_by_slot(strategy):
     """All-zero statistics give every key the score 0: the kept candidates must be
     the lowest slots (ties go to the lower slot)."""
     cfg = C["tiny"].replace(name="zero_stats", n_kv=3000, budget=900, sink=5, window=100, agg="max")
@@ -122,7 +150,7 @@ def test_zero_statistics_break_ties_by_slot():
     _check_oracle_compaction(prob, kept)
 
 
-def test_empty_and_zero_budget_units():
+def test_empty_and_zero_budget_units(strategy):
     cfg = C["batched_decode"].replace(name="empty", n_seqs=4, n_kv=700, ragged_min=100, window=0, sink=0)
     prob = DeviceProblem(cfg)
     prob.len[1] = 0
@@ -137,7 +165,7 @@ def test_empty_and_zero_budget_units():
         check_unit(prob, unit)
 
 
-def test_device_flags_record_bad_metadata():
+def test_device_flags_record_bad_metadata(strategy):
     """Out-of-contract device metadata is clamped by the kernels and reported."""
     cfg = C["batched_decode"].replace(name="flags", n_seqs=3, n_kv=500, ragged_min=200)
     prob = DeviceProblem(cfg)
