@@ -86,6 +86,28 @@ def cpu_baseline(cfg, seconds: float) -> dict:
             "host_cpus": os.cpu_count()}
 
 
+def recorded_traffic(cfg_name: str):
+    """k_score's HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if one exists and the kernel sources are the ones it measured;
+    else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_score_{cfg_name}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("tria_kernels.hip", "tria_kernels.h"):
+        with open(os.path.join(ROOT, "key_importance_scoring_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def copy_probe(gb: float, steps: int) -> int:
     """A plain copy of a known number of bytes (torch's copy kernel): its time gives the
     achievable streaming bandwidth, and its FETCH_SIZE / WRITE_SIZE counters the factor
@@ -223,8 +245,9 @@ def main() -> int:
                                     "region of the same K steps after the timed one",
                           "ms_per_step_with_kernel_events": ms_inst},
         "roofline": {"kernel": "k_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "dominant_kernel": dom},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(cfg.name),
+                     "algorithmic_bytes_per_launch": score_bytes, "dominant_kernel": dom},
         "cpu_baseline": base,
     }
     print(json.dumps(out))
