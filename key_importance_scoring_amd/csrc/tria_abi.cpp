@@ -228,7 +228,8 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
 
   tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->n_kv_heads, p->head_dim, p->n_layers, p->pairing,
                     std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean,
-                    p->group, L.n_tiles, B, reinterpret_cast<uint64_t*>(part), next_tile, hist, flags};
+                    p->group, L.n_tiles, tria::score_tile_keys(p->group), n_max, B,
+                    reinterpret_cast<uint64_t*>(part), next_tile, hist, flags};
   hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 

@@ -9,6 +9,9 @@ namespace tria {
 
 constexpr int kMaxOffsets = 256;
 constexpr int kMaxGroup = 8;
+// Up to this many units, the score kernel claims only tiles that hold keys (every
+// workgroup keeps all lengths and a prefix of the units' tiles in LDS).
+constexpr int kListUnits = 512;
 constexpr int kScoreTileMax = 2048;
 // keys per score tile: two tiles of scores ([G][tile + 16] fp32 each) live in LDS
 #ifndef TRIA_SCORE_TILE_SMALL_G
@@ -57,7 +60,8 @@ struct CoefArgs {
   const float* q_re;
   const float* q_im;
   const float* q_abs;
-  int32_t group, n_tiles;     // query heads per KV head; score tiles per (unit, KV head)
+  int32_t group, n_tiles, tile;  // query heads per KV head; score tiles per (unit, KV head), keys per tile
+  int32_t n_max;
   uint32_t* B;                // [U][Hkv][d/16][64] 16-byte MFMA B operands of k_score
   uint64_t* part;             // [U][Hq][n_tiles][3] tile moments of k_score, set to kUnpublished here
   int32_t* next_tile;         // tile claim counter of k_score, cleared here
@@ -127,7 +131,10 @@ struct CompactArgs {
   int32_t* flags;             // may be null
 };
 
-constexpr int kCompactRows = 64;   // kept rows per compaction workgroup
+#ifndef TRIA_COMPACT_ROWS
+#define TRIA_COMPACT_ROWS 64
+#endif
+constexpr int kCompactRows = TRIA_COMPACT_ROWS;   // kept rows per compaction workgroup
 
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s);

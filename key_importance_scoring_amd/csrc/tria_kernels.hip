@@ -162,8 +162,13 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   __shared__ float s_c[kMaxGroup * D];  // coefficient rows, pairing layout
   __shared__ float s_n[kMaxGroup * F];  // norm weights
 
+  // tiles past len[u] hold no keys: their moments are published here, as zeros
+  const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
   const int64_t per = (int64_t)G * a.n_tiles * 3;
-  for (int64_t i = t; i < per; i += 256) a.part[ug * per + i] = kUnpublished;
+  for (int64_t i = t; i < per; i += 256) {
+    const int tile = (int)((i / 3) % a.n_tiles);
+    a.part[ug * per + i] = (int64_t)tile * a.tile >= n_u ? 0ull : kUnpublished;
+  }
   for (int i = t; i < kBins; i += 256) a.hist[ug * kBins + i] = 0u;
   if (u == 0 && g == 0 && t == 0) *a.next_tile = 0;
 
@@ -267,6 +272,23 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
 }
 
 
+// Inclusive prefix sum over a workgroup of NT threads (wtot: NT / 64 slots).
+template <int NT>
+__device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wtot[wave] = v;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  __syncthreads();
+  return v + base;
+}
+
 // ============================================================================ k_score
 // re^2 + im^2 of a packed bf16 pair (re in the low half), products exact in fp32.
 // Kept as the builtin (not hand-written asm) so the compiler sees the instruction
@@ -337,12 +359,12 @@ struct TileInfo {
   int ug, u, g, tile, n, tile0, tlen;
 };
 
-// The tile's place; its length fields are filled by tile_len, which loads len[u]
-// (kept apart so that a tile's first loads need not wait for it).
-__device__ inline TileInfo tile_info(const ScoreArgs& a, int t) {
+// The tile's place; its length fields are filled by tile_len (kept apart so that a
+// tile's first loads need not wait for len[u]).
+__device__ inline TileInfo tile_info(const ScoreArgs& a, int ug, int tile) {
   TileInfo ti;
-  ti.tile = t % a.n_tiles;
-  ti.ug = t / a.n_tiles;
+  ti.tile = tile;
+  ti.ug = ug;
   ti.u = ti.ug / a.hkv;
   ti.g = ti.ug % a.hkv;
   ti.tile0 = ti.tile * a.tile;
@@ -358,7 +380,7 @@ __device__ inline void tile_len(const ScoreArgs& a, TileInfo& ti, int n_loaded, 
 // Scores one tile into LDS (s_raw, [G][tile + 16]), writes the per-query-head
 // scores if wanted, and publishes the tile's candidate moments.
 template <int D, int P, bool PAGED>
-__device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, float* s_raw, int* s_bt) {
+__device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known, float* s_raw, int* s_bt) {
   using S = Shape<D>;
   constexpr int NBI = stage_blocks<D>();
   constexpr int STAGE = 16 * NBI;  // keys per pipeline stage
@@ -372,10 +394,11 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, float* s_raw
   const int kpw = a.tile / 4;      // keys per wave
   const int u = ti.u, g = ti.g, tile0 = ti.tile0;
   const int kw0 = tile0 + wave * kpw;
-  // slots whose rows exist whatever len[u] is (a dense view is readable, and a paged
-  // view's table covers, n_max slots): the first stage is issued before len[u] arrives
-  const int kcap = min(kw0 + kpw, a.n_max);
-  const int n_loaded = a.len[u];   // first needed once the first two stages are in flight
+  // the slots the first stage may read: up to len[u] when it is known (n_known >= 0);
+  // else up to n_max (a dense view is readable, and a paged view's table covers, n_max
+  // slots), so that the first stage is issued before len[u] arrives
+  const int kcap = max(min(kw0 + kpw, n_known >= 0 ? n_known : a.n_max), min(kw0 + 1, a.n_max));
+  const int n_loaded = n_known >= 0 ? n_known : a.len[u];
 
   // ---- paged caches: the tile's block ids in LDS.  Ids of pages past len[u] may be
   // anything: load_stage maps an out-of-pool id to block 0, and only pages that
@@ -402,8 +425,8 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, float* s_raw
     }
   }
 
-  // the first stage, unconditionally and before len[u] is known: a wave past n_max
-  // (in the last tile) reloads row kcap - 1 = n_max - 1 >= tile0, which exists
+  // the first stage, unconditionally and possibly before len[u] is known: a wave with
+  // no keys reloads row kcap - 1, which is below n_max and at or past tile0
   Stage<D> cA, cB;
   load_stage<D, PAGED>(cA, a.k, u, g, kw0, kcap, col, grp, s_bt, page0);
 
@@ -556,14 +579,15 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, float* s_raw
 // GQA group onto the KV head [Fold note, sec. 4: normalize-then-max; mean is the
 // other variant] and writes the aggregate; protected slots (sinks, recent window)
 // get +inf.
-__device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, const float* s_raw, uint32_t* s_hist) {
+__device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_known, const float* s_raw,
+                                     uint32_t* s_hist) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = a.group;
   const int hq = a.hkv * G;
   const int RS = a.tile + 16;
   __shared__ float s_mean[kMaxGroup], s_inv[kMaxGroup];
-  tile_len(a, ti, a.len[ti.u], false);
+  tile_len(a, ti, n_known >= 0 ? n_known : a.len[ti.u], false);
 
   // the group's mean and standard deviation per query head, from every tile's
   // moments (fixed summation order: lane j takes tiles j, j + 64, ...; then a fixed
@@ -650,7 +674,10 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, const floa
 // order from a counter.  Each workgroup scores and publishes its current tile, and
 // only then finalises its previous one (two LDS score buffers): by that time the
 // previous tile's group has nearly always published, so the moment exchange hides
-// behind the streaming.  A workgroup waits only on tiles that are already
+// behind the streaming.  With at most kListUnits units every workgroup first reads
+// all lengths into LDS, and the claims run over the tiles that hold keys only (the
+// tiles of a (unit, KV head) still consecutive); k_coef has published empty tiles'
+// moments as zeros.  A workgroup waits only on tiles that are already
 // claimed-and-published or claimed by running workgroups that publish before they
 // wait; with P workgroups each holding at most two tiles, a circular wait would
 // need 2P <= n_tiles, and P >= n_tiles (the host checks it), so the wait always ends
@@ -664,19 +691,76 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   float* buf0 = s_dyn;
   float* buf1 = s_dyn + G * RS;
   int* s_bt = reinterpret_cast<int*>(s_dyn + 2 * G * RS);
-  const int total = a.n_units * a.hkv * a.n_tiles;
-  int prev = -1;
+  const int scratch = PAGED && a.tile + 1 > kBins ? a.tile + 1 : kBins;
+  int* s_len = s_bt + scratch;            // [kListUnits] lengths
+  int* s_pre = s_len + kListUnits;        // [kListUnits + 1] tiles of the units before
+  const int U = a.n_units;
+  const bool listed = U <= kListUnits;
+  int total = U * a.hkv * a.n_tiles;
+  if (listed) {
+    // thread t takes units [2t, 2t + 2): lengths, then the prefix of their tiles
+    __shared__ uint32_t wtot[4];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = 2 * threadIdx.x + k;
+      if (i < U) {
+        const int n = fix_len(a.len[i], a.n_max, a.flags);
+        s_len[i] = n;
+        cnt += (uint32_t)((n + a.tile - 1) / a.tile * a.hkv);
+      }
+    }
+    uint32_t run = block_scan_incl<256>(cnt, wtot) - cnt;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = 2 * threadIdx.x + k;
+      if (i < U) {
+        s_pre[i] = (int)run;
+        run += (uint32_t)((s_len[i] + a.tile - 1) / a.tile * a.hkv);
+      }
+    }
+    // the thread holding the last unit (or thread 0 when there is none) ends the prefix
+    if ((2 * (int)threadIdx.x < U && 2 * (int)threadIdx.x + 2 >= U) || (U == 0 && threadIdx.x == 0))
+      s_pre[U] = (int)run;
+    __syncthreads();
+    total = s_pre[U];
+  }
+  // claim index -> (unit x KV head, tile)
+  auto place = [&](int t, int& ug, int& tile) {
+    if (!listed) {
+      tile = t % a.n_tiles;
+      ug = t / a.n_tiles;
+      return;
+    }
+    int lo = 0, hi = U - 1;   // the last unit whose tiles start at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int r = t - s_pre[lo];
+    const int nt = (s_len[lo] + a.tile - 1) / a.tile;
+    ug = lo * a.hkv + r / nt;
+    tile = r % nt;
+  };
+  int pug = -1, ptile = 0;
   bool b = false;
   for (;;) {
     if (threadIdx.x == 0) s_t = atomicAdd(a.next_tile, 1);
     __syncthreads();
     const int t = s_t;
     __syncthreads();
-    if (t < total) score_phase<D, P, PAGED>(a, tile_info(a, t), b ? buf1 : buf0, s_bt);
+    int ug = 0, tile = 0;
+    if (t < total) {
+      place(t, ug, tile);
+      score_phase<D, P, PAGED>(a, tile_info(a, ug, tile), listed ? s_len[ug / a.hkv] : -1, b ? buf1 : buf0, s_bt);
+    }
     // s_bt served the current tile's score phase; finalize reuses it as histogram scratch
-    if (prev >= 0) finalize_tile(a, tile_info(a, prev), b ? buf0 : buf1, reinterpret_cast<uint32_t*>(s_bt));
+    if (pug >= 0)
+      finalize_tile(a, tile_info(a, pug, ptile), listed ? s_len[pug / a.hkv] : -1, b ? buf0 : buf1,
+                    reinterpret_cast<uint32_t*>(s_bt));
     if (t >= total) break;
-    prev = t;
+    pug = ug;
+    ptile = tile;
     b = !b;
   }
 }
@@ -700,23 +784,6 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
 __device__ inline uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);  // -0 -> +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Inclusive prefix sum over a workgroup of NT threads (wtot: NT / 64 slots).
-template <int NT>
-__device__ inline uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) wtot[wave] = v;
-  __syncthreads();
-  uint32_t base = 0;
-  for (int w = 0; w < wave; ++w) base += wtot[w];
-  __syncthreads();
-  return v + base;
 }
 
 // The bin whose cumulative count from the top first reaches krem (1 <= krem <=
@@ -1302,10 +1369,11 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
 
 size_t score_lds(int group, bool paged) {
   const int tile = score_tile_keys(group);
-  // two score buffers, then a region that holds the tile's block ids during the
-  // score phase and the aggregate histogram during finalisation
+  // two score buffers, a region that holds the tile's block ids during the score
+  // phase and the aggregate histogram during finalisation, and the units' lengths and
+  // tile prefix
   const size_t scratch = paged && tile + 1 > kBins ? (size_t)tile + 1 : (size_t)kBins;
-  return (size_t)2 * group * (tile + 16) * 4 + scratch * 4;
+  return (size_t)2 * group * (tile + 16) * 4 + scratch * 4 + (size_t)(2 * kListUnits + 1) * 4;
 }
 
 int score_capacity(int d, int pairing, bool paged, int group) {

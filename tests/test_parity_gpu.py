@@ -38,6 +38,9 @@ SMALL = {
     "all_protected": C["tiny"].replace(name="all_protected", n_kv=200, window=256, budget=300),
     "short_units": C["batched_decode"].replace(name="short_units", n_seqs=5, n_kv=40, ragged_min=1, window=8,
                                               sink=2, budget_frac=0.5),
+    # more units than the score kernel keeps lengths of in LDS: every tile is claimed
+    "many_units": C["batched_decode"].replace(name="many_units", n_seqs=520, n_kv_heads=2, n_kv=2200,
+                                             ragged_min=16, window=64, budget_frac=0.4),
 }
 
 
