@@ -99,6 +99,7 @@ struct SelState {
 #endif
 constexpr int kSelTile = TRIA_SEL_TILE; // slots per selection tile (kSelTile / 256 per thread)
 constexpr int kSelGroupMax = 32768;     // per-group selection: 512 threads x 64 slots in registers
+constexpr int kRefineLds = 3072;        // candidates the refinement keeps in LDS
 constexpr int kMaxSelTiles = 2048;      // per (unit, KV head): n_max <= 2048 kSelTile
 
 struct SelectArgs {

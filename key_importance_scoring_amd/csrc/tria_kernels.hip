@@ -933,6 +933,8 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   __shared__ uint32_t sh[2];
   __shared__ int32_t s_gtb[kMaxSelTiles], s_eqc[kMaxSelTiles];
   __shared__ int32_t s_pre[kMaxSelTiles + 1];   // candidates before each tile's segment
+  __shared__ uint32_t s_key[kRefineLds];        // candidates' order keys and slots, when
+  __shared__ int32_t s_slot[kRefineLds];        // they fit (else read again per pass)
 
   const SelState bd = a.st[ug];
   // candidate i lives in tile seg(i)'s segment, at position i - s_pre[seg(i)]
@@ -970,6 +972,18 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
 
   uint32_t T = 0, keq = 0;
   const bool refine = bd.b1 >= 0 && bd.b1 < kBins;
+  // candidate i's slot and key: from LDS when all fit, else from the list and agg
+  const bool staged = m <= kRefineLds;
+  if (refine && staged) {
+    for (int i = tid; i < m; i += 512) {
+      const int slot = cand(i);
+      s_slot[i] = slot;
+      s_key[i] = order_key(row[slot]);
+    }
+  }
+  __syncthreads();
+  auto cand_slot = [&](int i) { return staged ? s_slot[i] : cand(i); };
+  auto cand_key = [&](int i) { return staged ? s_key[i] : order_key(row[cand(i)]); };
   if (refine) {
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)bd.krem;
 #pragma unroll
@@ -979,7 +993,7 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
       for (int i = tid; i < nb; i += 512) hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < m; i += 512) {
-        const uint32_t key = order_key(row[cand(i)]);
+        const uint32_t key = cand_key(i);
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sft) & (nb - 1)], 1u);
       }
       __syncthreads();
@@ -1000,8 +1014,8 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   __syncthreads();
   if (refine) {
     for (int i = tid; i < m; i += 512) {
-      const int slot = cand(i);
-      const uint32_t key = order_key(row[slot]);
+      const int slot = cand_slot(i);
+      const uint32_t key = cand_key(i);
       if (key > T) atomicAdd(&s_gtb[slot / kSelTile], 1);
       else if (key == T) atomicAdd(&s_eqc[slot / kSelTile], 1);
     }
