@@ -38,7 +38,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # stream kinds for SeedSequence
-_K_CENTRE, _K_NOISE, _V_ROWS, _Q_STATS, _LENGTHS, _BLOCKS, _NONCONC = range(7)
+_K_CENTRE, _K_NOISE, _V_ROWS, _Q_STATS, _LENGTHS, _BLOCKS, _NONCONC, _Q_ROWS = range(8)
 
 
 @dataclass(frozen=True)
@@ -190,8 +190,9 @@ def key_centres(cfg: Config, layer: int, kv_head: int) -> np.ndarray:
     return c
 
 
+@functools.lru_cache(maxsize=8)
 def q_stats(cfg: Config):
-    """(q_mean_re, q_mean_im, q_abs_mean), each float32 [L][Hq][F]."""
+    """(q_mean_re, q_mean_im, q_abs_mean), each float32 [L][Hq][F] (read-only)."""
     F = cfg.head_dim // 2
     L, Hq = cfg.n_layers, cfg.n_q_heads
     re = np.zeros((L, Hq, F), np.float32)
@@ -212,6 +213,8 @@ def q_stats(cfg: Config):
             re[l, h] = mu.real
             im[l, h] = mu.imag
             ab[l, h] = absm
+    for x in (re, im, ab):
+        x.setflags(write=False)
     return re, im, ab
 
 
@@ -256,6 +259,28 @@ def key_rows(cfg: Config, unit: int, kv_head: int) -> np.ndarray:
     ra = a * cos - b * sin
     rb = a * sin + b * cos
     return f32_to_bf16_bits(_layout(ra, rb, cfg.pairing).astype(np.float32))
+
+
+def query_rows(cfg: Config, layer: int, q_head: int, n_tokens: int) -> np.ndarray:
+    """uint16 [n_tokens][d]: bf16 bits of a synthetic stream of pre-RoPE queries of one
+    (layer, query head), the input of calibration: each band is the head's centre
+    (the E[q_f] of q_stats) plus N(0, 0.3^2) per component, laid out per the pairing."""
+    re, im, _ = q_stats(cfg)
+    F = cfg.head_dim // 2
+    rng = _rng(cfg, _Q_ROWS, layer, q_head)
+    noise = rng.standard_normal((2, n_tokens, F)) * 0.3
+    a = re[layer, q_head][None, :].astype(np.float64) + noise[0]
+    b = im[layer, q_head][None, :].astype(np.float64) + noise[1]
+    return f32_to_bf16_bits(_layout(a, b, cfg.pairing).astype(np.float32))
+
+
+def query_stream(cfg: Config, n_tokens: int) -> np.ndarray:
+    """uint16 [L][Hq][n_tokens][d]: query_rows of every (layer, query head)."""
+    out = np.empty((cfg.n_layers, cfg.n_q_heads, n_tokens, cfg.head_dim), np.uint16)
+    for l in range(cfg.n_layers):
+        for h in range(cfg.n_q_heads):
+            out[l, h] = query_rows(cfg, l, h, n_tokens)
+    return out
 
 
 def value_rows(cfg: Config, unit: int, kv_head: int) -> np.ndarray:

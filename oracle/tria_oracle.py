@@ -36,6 +36,9 @@ reason in the design notes of the repository):
 * Budget B counts every kept slot, protected ones included; kept count is
   min(B, n).  Protected slots rank above every candidate; among equal
   aggregates the lower slot wins.  Kept slots are reported in ascending order.
+* Calibration: the concentration R_f is |E q_f| / E|q_f| (the ratio the norm
+  term's weight E|q_f| (1 - R_f) needs); the pages name it a mean resultant
+  length, whose circular-statistics form |E[q_f / |q_f|]| is returned beside it.
 
 Parity pins (tests/test_oracle_pins.py) tie each function below to closed forms,
 textbook routines, invariants or brute force.  No function here is left
@@ -291,3 +294,30 @@ def kth_threshold(agg: np.ndarray, n: int, budget: int, sink: int, window: int) 
     if need <= 0 or need > cand.size or min(budget, n) == n:
         return float("inf")
     return float(cand[need - 1])
+
+
+# ----------------------------------------------------------------------------- calibration
+
+def calibrate(q_bits: np.ndarray, pairing: str):
+    """Calibrated query statistics of one (layer, query head) from T pre-RoPE query
+    rows (bf16 bits [T][d]) [Calib issue, "How it works": per (layer, head, band)
+    E[Re q_c[f]], E[Im q_c[f]], E|q_c[f]|, in the model's pairing layout; Blog, the
+    calibration step: average the pre-RoPE queries per band].
+
+    Returns (mean_re, mean_im, abs_mean, r, mrl), each [d/2] float64:
+      r   = |E q_f| / E|q_f|            (0 where E|q_f| = 0): the concentration whose
+            complement weighs the norm term [Blog, The Method: (1 - R_f)];
+      mrl = |E[q_f / |q_f|]|            (q_f = 0 contributes 0): the circular mean
+            resultant length of the band's phases [Blog: R = 1 when all point the
+            same way, R = 0 when spread uniformly].
+    """
+    q = complex_bands(bf16_bits_to_f64(q_bits), pairing)          # [T][F]
+    if q.shape[0] == 0:
+        raise ValueError("no query rows")
+    mean = q.mean(axis=0)
+    mag = np.abs(q)
+    abs_mean = mag.mean(axis=0)
+    r = np.divide(np.abs(mean), abs_mean, out=np.zeros_like(abs_mean), where=abs_mean > 0)
+    unit = np.divide(q, mag, out=np.zeros_like(q), where=mag > 0)
+    mrl = np.abs(unit.mean(axis=0))
+    return mean.real, mean.imag, abs_mean, r, mrl

@@ -11,6 +11,7 @@ import math
 import os
 
 import numpy as np
+from scipy.stats import directional_stats
 import pytest
 import torch
 
@@ -373,3 +374,87 @@ def test_synthetic_keys_invert_to_their_centre():
     c = synth.key_centres(cfg, 0, 1)
     err = np.abs(k_pre.mean(axis=0) - c)
     assert np.max(err) < 0.05        # noise std 0.3 * sqrt(2) / sqrt(2048) ~ 0.01, plus bf16 rounding
+
+
+# ----------------------------------------------------------------------------- calibration
+
+def _bits(values):
+    """float values exactly representable in bf16 -> bf16 bit patterns."""
+    v = np.asarray(values, dtype=np.float32)
+    b = v.view(np.uint32)
+    assert ((b & 0xFFFF) == 0).all(), "not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def test_calibration_hand_values():
+    """One band (d = 2, NEOX): rows q = 2 and q = i.  E q = 1 + 0.5i, E|q| = 1.5, so
+    R = |1 + 0.5i| / 1.5; the unit phasors are 1 and i, so the circular mean
+    resultant length is |1 + i| / 2.  The two concentrations differ when the
+    magnitudes do."""
+    q = _bits([[2.0, 0.0], [0.0, 1.0]])
+    mre, mim, ab, r, mrl = o.calibrate(q, "neox")
+    assert mre[0] == 1.0 and mim[0] == 0.5 and ab[0] == 1.5
+    assert r[0] == pytest.approx(np.sqrt(1.25) / 1.5, rel=1e-15)
+    assert mrl[0] == pytest.approx(np.sqrt(0.5), rel=1e-15)
+
+
+def test_calibration_identical_and_opposite_rows():
+    rng = np.random.default_rng(5)
+    row = _bits(np.round(rng.normal(size=(1, 16)) * 64) / 64)
+    same = np.repeat(row, 9, axis=0)
+    mre, mim, ab, r, mrl = o.calibrate(same, "interleaved")
+    z = o.complex_bands(o.bf16_bits_to_f64(row), "interleaved")[0]
+    np.testing.assert_array_equal(mre + 1j * mim, z)
+    np.testing.assert_allclose(ab, np.abs(z), rtol=1e-15)
+    nz = np.abs(z) > 0
+    np.testing.assert_allclose(r[nz], 1.0, rtol=1e-15)
+    np.testing.assert_allclose(mrl[nz], 1.0, rtol=1e-15)
+    # a row and its negation: the centre cancels, the magnitudes do not
+    pair = np.concatenate([row, row ^ np.uint16(0x8000)])
+    mre, mim, ab, r, mrl = o.calibrate(pair, "interleaved")
+    np.testing.assert_array_equal(mre, 0.0)
+    np.testing.assert_array_equal(mim, 0.0)
+    np.testing.assert_allclose(ab, np.abs(z), rtol=1e-15)
+    np.testing.assert_array_equal(r, 0.0)
+    np.testing.assert_allclose(mrl, 0.0, atol=1e-15)
+
+
+def test_calibration_mrl_matches_scipy_directional_stats():
+    rng = np.random.default_rng(6)
+    q = rng.normal(size=(200, 32)) + 0.8
+    bits = (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # truncation: any bf16 values
+    _, _, _, _, mrl = o.calibrate(bits, "neox")
+    z = o.complex_bands(o.bf16_bits_to_f64(bits), "neox")
+    for f in range(16):
+        pts = np.stack([z[:, f].real, z[:, f].imag], axis=1)
+        ref = directional_stats(pts, normalize=True).mean_resultant_length
+        assert mrl[f] == pytest.approx(ref, rel=1e-12)
+
+
+def test_calibration_pairing_relabel_and_scaling():
+    """The same complex data laid out NEOX and interleaved gives the same statistics;
+    scaling the queries by 2 (exact in bf16) doubles the means and keeps both
+    concentrations."""
+    rng = np.random.default_rng(7)
+    F = 8
+    bands = np.round(rng.normal(size=(50, F, 2)) * 32) / 32
+    neox = _bits(np.concatenate([bands[:, :, 0], bands[:, :, 1]], axis=1))
+    inter = _bits(bands.reshape(50, 2 * F))
+    a = o.calibrate(neox, "neox")
+    b = o.calibrate(inter, "interleaved")
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    c = o.calibrate(_bits(2 * bands.reshape(50, 2 * F)), "interleaved")
+    np.testing.assert_allclose(c[0], 2 * b[0], rtol=1e-15)
+    np.testing.assert_allclose(c[2], 2 * b[2], rtol=1e-15)
+    np.testing.assert_allclose(c[3], b[3], rtol=1e-14)
+    np.testing.assert_allclose(c[4], b[4], rtol=1e-14)
+    assert (b[3] <= 1 + 1e-15).all() and (b[4] <= 1 + 1e-15).all()
+
+
+def test_calibration_feeds_the_norm_weight():
+    """E|q_f| (1 - R_f) is the norm weight E|q_f| - |E q_f| the scorer takes."""
+    rng = np.random.default_rng(8)
+    q = _bits(np.round(rng.normal(size=(64, 16)) * 16) / 16 + 0.5)
+    mre, mim, ab, r, _ = o.calibrate(q, "neox")
+    np.testing.assert_allclose(ab * (1 - r), ab - np.abs(mre + 1j * mim), atol=1e-15)
