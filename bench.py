@@ -6,6 +6,10 @@ One step = tria_score -> tria_select -> tria_compact over the whole workload
 line.  Default workload: Qwen3-8B-shaped, 36 layers x 8 KV heads x 32768 keys.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config qwen3_8b]
+
+With --calibrate it times the calibration reduction instead (tria_calibrate over a
+Qwen3-8B-shaped stream of 8192 pre-RoPE query rows per layer and query head) and
+prints that measurement's JSON line.
 """
 from __future__ import annotations
 
@@ -132,11 +136,137 @@ def copy_probe(gb: float, steps: int) -> int:
     return 0
 
 
+CALIB_METRIC = "G pre-RoPE query rows reduced to calibration statistics/s; % of HBM peak GB/s"
+
+
+def calib_cpu_baseline(cfg, T: int, seconds: float) -> dict:
+    """oracle.calibrate as it stands on whole (layer, query head) streams, in order,
+    until `seconds` of oracle time have passed."""
+    from threadpoolctl import threadpool_limits
+    from key_importance_scoring_amd import synth
+    from oracle import tria_oracle as o
+
+    rows = 0
+    spent = 0.0
+    heads = 0
+    with threadpool_limits(1):
+        for l in range(cfg.n_layers):
+            for h in range(cfg.n_q_heads):
+                q = synth.query_rows(cfg, l, h, T)
+                t0 = time.perf_counter()
+                o.calibrate(q, cfg.pairing)
+                spent += time.perf_counter() - t0
+                rows += T
+                heads += 1
+                if spent >= seconds:
+                    break
+            if spent >= seconds:
+                break
+    return {"value": rows / spent / 1e9, "unit": "G rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} (layer, query head) streams of {T} rows of {cfg.name}, fp64, "
+                      f"{spent:.1f} s on one host thread",
+            "host_cpus": os.cpu_count()}
+
+
+def bench_calibrate(args) -> int:
+    """The calibration reduction: tria_calibrate over a [L][Hq][T][d] stream of
+    pre-RoPE query rows resident in HBM."""
+    import numpy as np
+    import torch
+    from key_importance_scoring_amd import _lib as L
+    from key_importance_scoring_amd import synth
+    from key_importance_scoring_amd.device import calibrate, params_for
+
+    cfg = synth.CONFIGS[args.config]
+    T = args.tokens
+    print(f"[bench] building the {cfg.name} query stream, {T} tokens", file=sys.stderr, flush=True)
+    q = None
+    path = ""
+    if args.input_cache:
+        os.makedirs(args.input_cache, exist_ok=True)
+        path = os.path.join(args.input_cache, f"{cfg.name}_s{cfg.seed}_q{T}.npy")
+        if os.path.exists(path):
+            q = np.load(path, mmap_mode="r")
+    if q is None:
+        q = synth.query_stream(cfg, T)
+        if path:
+            np.save(path, q)
+    qd = torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).to("cuda:0")
+    del q
+    p = params_for(cfg)
+    stream = torch.cuda.current_stream()
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    out = calibrate(p, qd, stream=stream)        # also the copy the timed outputs must equal
+    for _ in range(args.warmup - 1):
+        calibrate(p, qd, stream=stream)
+    torch.cuda.synchronize()
+    # outputs and workspace allocated once; the timed region is the entry point alone
+    F = cfg.head_dim // 2
+    ws_bytes = L.tria_calibrate_workspace_size(p, T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    o5 = [torch.empty((cfg.n_layers, cfg.n_q_heads, F), dtype=torch.float32, device="cuda:0") for _ in range(5)]
+
+    def step():
+        L.tria_calibrate(p, qd, qd.stride(0), qd.stride(1), qd.stride(2), T, *o5, ws, ws_bytes, stream)
+
+    def region(kernel_events: bool):
+        L.tria_timing_read()
+        L.tria_timing_enable(kernel_events)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        L.tria_timing_enable(False)
+        return t0.elapsed_time(t1) / args.steps, L.tria_timing_read()
+
+    ms, _ = region(False)
+    ms_inst, kt = region(True)
+    for a, b in zip(o5, (out["q_mean_re"], out["q_mean_im"], out["q_abs_mean"], out["r"], out["mrl"])):
+        assert torch.equal(a, b)
+    rows = cfg.n_layers * cfg.n_q_heads * T
+    # algorithmic bytes: every query row read once, five fp32 statistics per band written
+    alg = rows * cfg.head_dim * 2 + 5 * cfg.n_layers * cfg.n_q_heads * F * 4
+    kms = kt["k_calib"][0] / kt["k_calib"][1]
+    achieved = alg / (kms / 1e3) / 1e9
+    print(f"[bench] {ms:.4f} ms/step ({ms_inst:.4f} with events), k_calib + k_calib_final {kms:.4f} ms",
+          file=sys.stderr, flush=True)
+    base = calib_cpu_baseline(cfg, T, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    print(json.dumps({
+        "metric": CALIB_METRIC,
+        "value": rows / (ms / 1e3) / 1e9,
+        "unit": "G rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"calibrate_{cfg.name}", "layers": cfg.n_layers, "q_heads": cfg.n_q_heads,
+                   "head_dim": cfg.head_dim, "tokens": T, "pairing": cfg.pairing},
+        "hbm_algorithmic_GBps": alg / (ms / 1e3) / 1e9,
+        "hbm_pct_of_peak": 100.0 * alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": alg,
+        "kernel_ms": {"k_calib+k_calib_final": kms},
+        "roofline": {"kernel": "k_calib (with k_calib_final)", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg},
+        "cpu_baseline": base,
+    }))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 20; 200 with --calibrate)")
+    ap.add_argument("--warmup", type=int, default=None, help="warmup steps (default 3; 50 with --calibrate)")
     ap.add_argument("--config", default="qwen3_8b")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--input-cache", default="", metavar="DIR",
@@ -144,7 +274,16 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GB",
                     help="instead of the pass, time a plain device-to-device copy of GB gigabytes "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="instead of the pass, time the calibration reduction (tria_calibrate) over a "
+                         "synthetic pre-RoPE query stream of --tokens rows per (layer, query head)")
+    ap.add_argument("--tokens", type=int, default=8192, help="calibration tokens (with --calibrate)")
     args = ap.parse_args()
+    # a calibration step is ~0.4 ms: more of them keep the timed region near 0.1 s
+    if args.steps is None:
+        args.steps = 200 if args.calibrate else 20
+    if args.warmup is None:
+        args.warmup = 50 if args.calibrate else 3
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the pass shards with no "
               f"exchange, so N GPUs run N independent copies of this measurement)", file=sys.stderr)
@@ -153,6 +292,8 @@ def main() -> int:
     import torch
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe, args.steps)
+    if args.calibrate:
+        return bench_calibrate(args)
     from key_importance_scoring_amd import _lib as L
     from key_importance_scoring_amd import synth
     from key_importance_scoring_amd.device import DeviceProblem

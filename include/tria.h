@@ -214,6 +214,43 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
                          const tria_kv_view* k_dst, const tria_kv_view* v_dst, int32_t* pos_dst,
                          void* stream);
 
+/* tria_calibrate - the calibrated query statistics tria_score reads, from a stream
+ * of pre-RoPE query rows [Calib issue, "How it works": per (layer, head, band)
+ * means in the RoPE complex pairing; Blog, the calibration step].
+ *
+ * For layer l < L = p->n_layers, query head h < Hq = p->n_kv_heads * p->group
+ * and band f < d/2, over the n_tokens rows q[l][h][t] (bf16, bands in
+ * p->pairing's layout):
+ *   q_mean_re[l][h][f]  = mean_t Re q_f      q_mean_im[l][h][f] = mean_t Im q_f
+ *   q_abs_mean[l][h][f] = mean_t |q_f|
+ *   r[l][h][f]   = |mean_t q_f| / mean_t |q_f|  (0 where mean_t |q_f| = 0); the
+ *                  concentration whose complement weighs the norm term
+ *   mrl[l][h][f] = |mean_t q_f / |q_f||          (q_f = 0 contributes 0); the
+ *                  circular mean resultant length of the band's phases
+ * The first three are tria_score's statistics arguments as they are.
+ *   q           [device] bf16; row (l, h, t) starts at element
+ *               l*stride_layer + h*stride_head + t*stride_token (each stride a
+ *               multiple of 8 elements, q 16-byte aligned)
+ *   n_tokens    >= 1
+ *   q_mean_re, q_mean_im, q_abs_mean
+ *               [device] fp32 [L][Hq][d/2]
+ *   r, mrl      [device] fp32 [L][Hq][d/2], or NULL when not wanted
+ *   ws          [device] workspace of ws_bytes >= tria_calibrate_workspace_size
+ * Sums run in fp32 over chunks of 1024 tokens, then in fp64 over the chunks in a
+ * fixed order: the results do not depend on the launch or on the strides.
+ * p->offsets, rope_base, sink, window and agg are not used (but must be valid).
+ * Inputs must be finite.  The call only enqueues work on `stream` (no
+ * synchronisation); outputs and ws must not be in use by other work meanwhile.
+ * Errors: TRIA_EINVAL (bad params, n_tokens < 1, a required pointer NULL),
+ * TRIA_ESHAPE (q or a stride not aligned as above, a negative stride, more than
+ * 65535 (layer, query head) pairs), TRIA_EWORKSPACE, TRIA_ELAUNCH.
+ */
+/* Bytes of workspace tria_calibrate needs (0 for invalid params or n_tokens < 1). */
+size_t tria_calibrate_workspace_size(const tria_params* p, int32_t n_tokens);
+tria_status tria_calibrate(const tria_params* p, const void* q, int64_t stride_layer, int64_t stride_head,
+                           int64_t stride_token, int32_t n_tokens, float* q_mean_re, float* q_mean_im,
+                           float* q_abs_mean, float* r, float* mrl, void* ws, size_t ws_bytes, void* stream);
+
 /* Caps the number of workgroups tria_score's persistent kernel launches (0, the
  * default, means as many as the device holds at once), for callers that keep
  * compute units free for work on other streams.  A cap below the score tiles of

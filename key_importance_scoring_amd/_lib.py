@@ -22,7 +22,8 @@ FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC 
 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
            "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name",
-           "tria_score_max_workgroups", "tria_select_strategy")
+           "tria_score_max_workgroups", "tria_select_strategy", "tria_calibrate_workspace_size",
+           "tria_calibrate")
 
 
 class TriaError(RuntimeError):
@@ -89,6 +90,11 @@ def load() -> ctypes.CDLL:
     lib.tria_score_max_workgroups.argtypes = [c_int32]
     lib.tria_select_strategy.restype = c_int32
     lib.tria_select_strategy.argtypes = [c_int32]
+    lib.tria_calibrate_workspace_size.restype = c_size_t
+    lib.tria_calibrate_workspace_size.argtypes = [POINTER(TriaParams), c_int32]
+    lib.tria_calibrate.restype = c_int32
+    lib.tria_calibrate.argtypes = [POINTER(TriaParams), c_void_p, c_int64, c_int64, c_int64, c_int32,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     _lib = lib
     return lib
 
@@ -160,6 +166,17 @@ def tria_compact(p: TriaParams, k_src: TriaKvView, v_src: TriaKvView, pos_src, p
     _check(load().tria_compact(ctypes.byref(p), ctypes.byref(k_src), ctypes.byref(v_src), ptr(pos_src), pos_heads,
                                n_units, n_max, b_max, ptr(len_), ptr(idx), ptr(cnt), ctypes.byref(k_dst),
                                ctypes.byref(v_dst), ptr(pos_dst), stream_handle(stream)))
+
+
+def tria_calibrate_workspace_size(p: TriaParams, n_tokens: int) -> int:
+    return int(load().tria_calibrate_workspace_size(ctypes.byref(p), n_tokens))
+
+
+def tria_calibrate(p: TriaParams, q, stride_layer: int, stride_head: int, stride_token: int, n_tokens: int,
+                   q_mean_re, q_mean_im, q_abs_mean, r, mrl, ws, ws_bytes: int, stream=None) -> None:
+    _check(load().tria_calibrate(ctypes.byref(p), ptr(q), stride_layer, stride_head, stride_token, n_tokens,
+                                 ptr(q_mean_re), ptr(q_mean_im), ptr(q_abs_mean), ptr(r), ptr(mrl), ptr(ws),
+                                 ws_bytes, stream_handle(stream)))
 
 
 def tria_device_flags(ws, stream=None) -> int:

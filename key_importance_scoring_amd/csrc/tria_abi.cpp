@@ -28,8 +28,8 @@ tria_status fail(tria_status s, const char* fmt, ...) {
 }
 
 // ------------------------------------------------------------------ timing
-enum { kIdCoef = 0, kIdScore, kIdSelect, kIdCompact, kNumIds };
-const char* const kNames[kNumIds] = {"k_coef", "k_score", "k_select", "k_compact"};
+enum { kIdCoef = 0, kIdScore, kIdSelect, kIdCompact, kIdCalib, kNumIds };
+const char* const kNames[kNumIds] = {"k_coef", "k_score", "k_select", "k_compact", "k_calib"};
 
 struct Rec {
   int id;
@@ -323,6 +323,40 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
                        n_units, n_max, b_max, hkv, d, n_rtiles, len, idx, cnt, nullptr};
   hipError_t e = timed(kIdCompact, s, [&] { return tria::launch_compact(ca, s); });
   return launch_status(e, "k_compact");
+}
+
+size_t tria_calibrate_workspace_size(const tria_params* p, int32_t n_tokens) {
+  if (check_params(p) != TRIA_OK || n_tokens < 1) return 0;
+  const size_t lh = (size_t)p->n_layers * p->n_kv_heads * p->group;
+  const size_t chunks = ((size_t)n_tokens + tria::kCalibChunk - 1) / tria::kCalibChunk;
+  return al256(lh * chunks * (size_t)(p->head_dim / 2) * 5 * sizeof(float));
+}
+
+tria_status tria_calibrate(const tria_params* p, const void* q, int64_t stride_layer, int64_t stride_head,
+                           int64_t stride_token, int32_t n_tokens, float* q_mean_re, float* q_mean_im,
+                           float* q_abs_mean, float* r, float* mrl, void* ws, size_t ws_bytes, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_tokens < 1) return fail(TRIA_EINVAL, "n_tokens %d < 1", n_tokens);
+  if (!q || !q_mean_re || !q_mean_im || !q_abs_mean) return fail(TRIA_EINVAL, "a required device pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(q) % 16) return fail(TRIA_ESHAPE, "q not 16-byte aligned");
+  if (stride_layer < 0 || stride_head < 0 || stride_token < 0)
+    return fail(TRIA_ESHAPE, "q has a negative stride");
+  if (stride_layer % 8 || stride_head % 8 || stride_token % 8)
+    return fail(TRIA_ESHAPE, "q strides must be multiples of 8 elements");
+  const int64_t lh = (int64_t)p->n_layers * p->n_kv_heads * p->group;
+  if (lh > 65535) return fail(TRIA_ESHAPE, "n_layers x query heads = %lld exceeds 65535", (long long)lh);
+  if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(TRIA_EWORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = tria_calibrate_workspace_size(p, n_tokens);
+  if (ws_bytes < need) return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  const int32_t n_chunks = (n_tokens + tria::kCalibChunk - 1) / tria::kCalibChunk;
+  tria::CalibArgs ca{static_cast<const uint16_t*>(q), stride_layer, stride_head, stride_token, p->n_layers,
+                     p->n_kv_heads * p->group, p->head_dim, p->pairing, n_tokens, n_chunks,
+                     static_cast<float*>(ws), q_mean_re, q_mean_im, q_abs_mean, r, mrl};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(kIdCalib, s, [&] { return tria::launch_calibrate(ca, s); });
+  return launch_status(e, "k_calib");
 }
 
 tria_status tria_device_flags(void* ws, int32_t* flags, void* stream) {

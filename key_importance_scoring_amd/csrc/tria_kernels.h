@@ -119,6 +119,20 @@ struct SelectArgs {
   int32_t* flags;
 };
 
+constexpr int kCalibChunk = 1024;       // query rows per calibration workgroup
+
+struct CalibArgs {
+  const uint16_t* q;
+  int64_t sl, sh, st;         // element strides: layer, query head, token
+  int32_t n_layers, hq, d, pairing, n_tokens, n_chunks;
+  float* part;                // [L][Hq][n_chunks][d/2][5] fp32 chunk sums (chunks of kCalibChunk rows)
+  float* mean_re;
+  float* mean_im;
+  float* abs_mean;
+  float* r;                   // may be null
+  float* mrl;                 // may be null
+};
+
 struct CompactArgs {
   KView ks, vs;
   MutKView kd, vd;
@@ -145,5 +159,6 @@ int score_capacity(int d, int pairing, bool paged, int group);
 // strategy: 0 automatic, 1 per group (when n_max fits), 2 tiled
 hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 
 }  // namespace tria

@@ -1362,6 +1362,152 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a) {
   }
 }
 
+// ============================================================================ calibration
+// tria_calibrate: per (layer, query head, band) means of Re q_f, Im q_f, |q_f| and of
+// the unit phasor q_f / |q_f| over a stream of pre-RoPE query rows [Calib issue,
+// "How it works"].  k_calib: workgroup (chunk, layer x head) sums kCalibChunk rows in
+// fp32.  Lane p of a row owns bands 8p .. 8p + 7 and loads both parts of them itself:
+// in NEOX rows the real parts at elements [8p, 8p + 8) and the imaginary parts d/2
+// further on, in interleaved rows the 16 elements [16p, 16p + 16).  The next rows'
+// loads are issued before the current rows' sums.  k_calib_final adds the chunks in
+// fp64, in chunk order, and divides.
+
+// Adds one band's contributions: re, im, |q|, re / |q|, im / |q| (0, 0 for q = 0).
+// The band is scaled by a power of two to a magnitude in [0.5, 1) before squaring, so
+// that no finite bf16 value overflows or loses precision to underflow; one reciprocal
+// square root (1 ulp) then gives both |q| and the unit phasor.  A nonzero m2 lies in
+// [0.25, 2), where adding 2^-100 changes nothing; for q = 0 the addition keeps the
+// reciprocal square root finite and every contribution 0.
+__device__ inline void calib_band(float re, float im, float (&acc)[5]) {
+  const int e = __builtin_amdgcn_frexp_expf(fabsf(re) > fabsf(im) ? re : im);   // of the larger part
+  const float a = __builtin_amdgcn_ldexpf(re, -e), b = __builtin_amdgcn_ldexpf(im, -e);
+  const float m2 = fmaf(a, a, b * b);                      // in [0.25, 2), or 0
+  const float r = __builtin_amdgcn_rsqf(m2 + 0x1p-100f);
+  acc[0] += re;
+  acc[1] += im;
+  acc[2] += __builtin_amdgcn_ldexpf(m2 * r, e);
+  acc[3] = fmaf(a, r, acc[3]);
+  acc[4] = fmaf(b, r, acc[4]);
+}
+
+// A lane's rows of one chunk: t0, t0 + RPP, ... (NR of them), in batches of NB whose
+// loads are issued one batch ahead of the sums.  FULL: every row exists.  Otherwise
+// rows at or past t1 load row t1 - 1 (a valid address) and count as zero.
+template <int D, int P, int NR, int NB, int RPP, bool FULL>
+__device__ inline void calib_rows(const uint16_t* base, int64_t st, int t0, int t1, int e0, int e1,
+                                  float (&acc)[8][5]) {
+  auto load = [&](u32x4 (&w)[NB][2], int b) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = t0 + (b + j) * RPP;
+      const uint16_t* row = base + (int64_t)(FULL ? t : min(t, t1 - 1)) * st;
+      w[j][0] = *reinterpret_cast<const u32x4*>(row + e0);
+      w[j][1] = *reinterpret_cast<const u32x4*>(row + e1);
+    }
+    // keep the batch's loads ahead of the previous batch's sums
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sums = [&](const u32x4 (&w)[NB][2], int b) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bool live = FULL || t0 + (b + j) * RPP < t1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t wr, wi;
+        bool hi;
+        if (P == 0) {      // real parts in piece 0, imaginary parts in piece 1
+          wr = w[j][0][k / 2];
+          wi = w[j][1][k / 2];
+          hi = k & 1;
+        } else {           // (re, im) pairs, four per piece
+          wr = wi = w[j][k / 4][k % 4];
+          hi = false;
+        }
+        if (!FULL) {
+          wr = live ? wr : 0u;
+          wi = live ? wi : 0u;
+        }
+        const float re = hi ? bf_hi(wr) : bf_lo(wr);
+        const float im = (P == 0 && !hi) ? bf_lo(wi) : bf_hi(wi);
+        calib_band(re, im, acc[k]);
+      }
+    }
+  };
+  static_assert(NR % (2 * NB) == 0, "rows per lane");
+  u32x4 wa[NB][2], wb[NB][2];
+  load(wa, 0);
+#pragma unroll 1
+  for (int b = 0; b < NR - 2 * NB; b += 2 * NB) {
+    load(wb, b + NB);
+    sums(wa, b);
+    load(wa, b + 2 * NB);
+    sums(wb, b + NB);
+  }
+  load(wb, NR - NB);
+  sums(wa, NR - 2 * NB);
+  sums(wb, NR - NB);
+}
+
+template <int D, int P>
+__global__ __launch_bounds__(256) void k_calib(CalibArgs a) {
+  constexpr int LPR = D / 16, RPP = 256 / LPR, F = D / 2;
+  constexpr int NR = kCalibChunk / RPP, NB = 2;    // rows per lane, rows per batch
+  const int chunk = blockIdx.x, lh = blockIdx.y;
+  const int l = lh / a.hq, h = lh % a.hq;
+  const int tid = threadIdx.x, p = tid % LPR, r0 = tid / LPR;
+  // element offsets of the lane's two 16-byte pieces within a row
+  const int e0 = P == 0 ? 8 * p : 16 * p, e1 = P == 0 ? F + 8 * p : 16 * p + 8;
+  const uint16_t* base = a.q + (int64_t)l * a.sl + (int64_t)h * a.sh;
+  const int t0 = chunk * kCalibChunk + r0;
+  float acc[8][5];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int s = 0; s < 5; ++s) acc[k][s] = 0.0f;
+  if ((chunk + 1) * kCalibChunk <= a.n_tokens)
+    calib_rows<D, P, NR, NB, RPP, true>(base, a.st, t0, a.n_tokens, e0, e1, acc);
+  else
+    calib_rows<D, P, NR, NB, RPP, false>(base, a.st, t0, a.n_tokens, e0, e1, acc);
+
+  // the rows of a pass share their bands: add them in row order through LDS
+  __shared__ float s_acc[RPP][F * 5];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int s = 0; s < 5; ++s) s_acc[r0][(8 * p + k) * 5 + s] = acc[k][s];
+  __syncthreads();
+  float* out = a.part + ((size_t)lh * a.n_chunks + chunk) * F * 5;
+  for (int i = tid; i < F * 5; i += 256) {
+    float v = 0.0f;
+#pragma unroll 8
+    for (int r = 0; r < RPP; ++r) v += s_acc[r][i];
+    out[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_calib_final(CalibArgs a) {
+  const int lh = blockIdx.x, F = a.d / 2, FV = F * 5;
+  __shared__ double s_sum[128 * 5];
+  const float* pp = a.part + (size_t)lh * a.n_chunks * FV;
+  for (int i = threadIdx.x; i < FV; i += 256) {
+    double v = 0.0;
+    for (int c = 0; c < a.n_chunks; ++c) v += (double)pp[(size_t)c * FV + i];
+    s_sum[i] = v;
+  }
+  __syncthreads();
+  const int f = threadIdx.x;
+  if (f >= F) return;
+  const double* sf = s_sum + 5 * f;
+  const double T = (double)a.n_tokens;
+  const double mr = sf[0] / T, mi = sf[1] / T, ab = sf[2] / T;
+  const size_t o = (size_t)lh * F + f;
+  a.mean_re[o] = (float)mr;
+  a.mean_im[o] = (float)mi;
+  a.abs_mean[o] = (float)ab;
+  if (a.r) a.r[o] = ab > 0.0 ? (float)(sqrt(mr * mr + mi * mi) / ab) : 0.0f;
+  if (a.mrl) a.mrl[o] = (float)(sqrt(sf[3] * sf[3] + sf[4] * sf[4]) / T);
+}
+
 // ============================================================================ launches
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   if (a.n_units == 0) return hipSuccess;
@@ -1501,6 +1647,27 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   // K and V in different layouts: one row at a time
   hipLaunchKernelGGL(k_compact, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s) {
+  if (a.n_layers == 0 || a.hq == 0 || a.n_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_chunks, (unsigned)(a.n_layers * a.hq));
+#define TRIA_CALIB_CASE(DD, PP)                                                 \
+  if (a.d == DD && a.pairing == PP) {                                          \
+    hipLaunchKernelGGL((k_calib<DD, PP>), grid, dim3(256), 0, s, a);           \
+    hipError_t e = hipGetLastError();                                          \
+    if (e != hipSuccess) return e;                                             \
+    hipLaunchKernelGGL(k_calib_final, dim3((unsigned)(a.n_layers * a.hq)), dim3(256), 0, s, a); \
+    return hipGetLastError();                                                  \
+  }
+  TRIA_CALIB_CASE(64, 0)
+  TRIA_CALIB_CASE(64, 1)
+  TRIA_CALIB_CASE(128, 0)
+  TRIA_CALIB_CASE(128, 1)
+  TRIA_CALIB_CASE(256, 0)
+  TRIA_CALIB_CASE(256, 1)
+#undef TRIA_CALIB_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tria

@@ -167,3 +167,25 @@ class DeviceProblem:
 
     def head_keys(self) -> int:
         return int(self.units.lengths.astype(np.int64).sum()) * self.cfg.n_kv_heads
+
+
+def calibrate(params: L.TriaParams, q: torch.Tensor, want_r: bool = True, want_mrl: bool = True,
+              stream=None) -> dict:
+    """tria_calibrate over a device tensor q [L][Hq][T][d] (bf16 or its 16-bit pattern;
+    any strides that are multiples of 8 elements, unit stride along d).  Allocates the
+    outputs and the workspace; returns {"q_mean_re", "q_mean_im", "q_abs_mean", "r",
+    "mrl"} as fp32 [L][Hq][d/2] device tensors (r, mrl None when not wanted)."""
+    if q.dim() != 4 or q.element_size() != 2 or q.stride(3) != 1:
+        raise ValueError("q must be a 16-bit [L][Hq][T][d] tensor with unit stride along d")
+    Ln, Hq, T, d = q.shape
+    F = d // 2
+    dev = q.device
+    out = {k: torch.empty((Ln, Hq, F), dtype=torch.float32, device=dev)
+           for k in ("q_mean_re", "q_mean_im", "q_abs_mean")}
+    out["r"] = torch.empty((Ln, Hq, F), dtype=torch.float32, device=dev) if want_r else None
+    out["mrl"] = torch.empty((Ln, Hq, F), dtype=torch.float32, device=dev) if want_mrl else None
+    ws_bytes = L.tria_calibrate_workspace_size(params, T)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    L.tria_calibrate(params, q, q.stride(0), q.stride(1), q.stride(2), T, out["q_mean_re"], out["q_mean_im"],
+                     out["q_abs_mean"], out["r"], out["mrl"], ws, ws_bytes, stream)
+    return out

@@ -274,12 +274,18 @@ def query_rows(cfg: Config, layer: int, q_head: int, n_tokens: int) -> np.ndarra
     return f32_to_bf16_bits(_layout(a, b, cfg.pairing).astype(np.float32))
 
 
-def query_stream(cfg: Config, n_tokens: int) -> np.ndarray:
-    """uint16 [L][Hq][n_tokens][d]: query_rows of every (layer, query head)."""
+def _query_job(args):
+    cfg, layer, q_head, n_tokens = args
+    return layer, q_head, query_rows(cfg, layer, q_head, n_tokens)
+
+
+def query_stream(cfg: Config, n_tokens: int, workers: int | None = None) -> np.ndarray:
+    """uint16 [L][Hq][n_tokens][d]: query_rows of every (layer, query head); drawn in a
+    process pool as iter_chunks does."""
     out = np.empty((cfg.n_layers, cfg.n_q_heads, n_tokens, cfg.head_dim), np.uint16)
-    for l in range(cfg.n_layers):
-        for h in range(cfg.n_q_heads):
-            out[l, h] = query_rows(cfg, l, h, n_tokens)
+    jobs = [(cfg, l, h, n_tokens) for l in range(cfg.n_layers) for h in range(cfg.n_q_heads)]
+    for l, h, rows in _run_jobs(_query_job, jobs, workers):
+        out[l, h] = rows
     return out
 
 
@@ -336,15 +342,10 @@ def _jobs(cfg: Config, which: str):
     return [(cfg, which, u, g) for u in range(cfg.n_units) for g in range(cfg.n_kv_heads)]
 
 
-def iter_chunks(cfg: Config, which: str, workers: int | None = None):
-    """Yield (unit, kv_head, rows) for every chunk of the K (``"k"``) or V (``"v"``) cache.
-
-    With ``workers > 1`` the chunks are drawn in a spawned process pool (no GPU state
-    is inherited); the order of the yielded chunks is then arbitrary.  The default
-    pool size can be set with the environment variable TRIA_SYNTH_WORKERS (1 keeps
-    everything in-process, e.g. under a profiler that attaches to every process).
-    """
-    jobs = _jobs(cfg, which)
+def _run_jobs(fn, jobs, workers: int | None):
+    """Yield fn(job) for every job, in a spawned process pool when workers > 1 (in an
+    arbitrary order then).  workers = None: TRIA_SYNTH_WORKERS, else up to 16 processes
+    for more than 16 jobs."""
     if workers is None:
         env = os.environ.get("TRIA_SYNTH_WORKERS")
         if env:
@@ -353,12 +354,23 @@ def iter_chunks(cfg: Config, which: str, workers: int | None = None):
             workers = min(16, os.cpu_count() or 1) if len(jobs) > 16 else 1
     if workers <= 1:
         for j in jobs:
-            yield _chunk_job(j)
+            yield fn(j)
         return
     import multiprocessing as mp
     with mp.get_context("spawn").Pool(workers) as pool:
-        for item in pool.imap_unordered(_chunk_job, jobs, chunksize=2):
+        for item in pool.imap_unordered(fn, jobs, chunksize=2):
             yield item
+
+
+def iter_chunks(cfg: Config, which: str, workers: int | None = None):
+    """Yield (unit, kv_head, rows) for every chunk of the K (``"k"``) or V (``"v"``) cache.
+
+    With ``workers > 1`` the chunks are drawn in a spawned process pool (no GPU state
+    is inherited); the order of the yielded chunks is then arbitrary.  The default
+    pool size can be set with the environment variable TRIA_SYNTH_WORKERS (1 keeps
+    everything in-process, e.g. under a profiler that attaches to every process).
+    """
+    yield from _run_jobs(_chunk_job, _jobs(cfg, which), workers)
 
 
 def dense_shape(cfg: Config):

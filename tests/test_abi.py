@@ -72,9 +72,9 @@ def test_strerror_and_kernel_names():
     for s in range(7):
         assert lib.tria_strerror(s)
     assert lib.tria_strerror(99) == b"unknown status"
-    names = [lib.tria_kernel_name(i) for i in range(4)]
-    assert names == [b"k_coef", b"k_score", b"k_select", b"k_compact"]
-    assert lib.tria_kernel_name(4) == b""
+    names = [lib.tria_kernel_name(i) for i in range(5)]
+    assert names == [b"k_coef", b"k_score", b"k_select", b"k_compact", b"k_calib"]
+    assert lib.tria_kernel_name(5) == b""
 
 
 def test_workspace_size_grows_with_the_problem():
@@ -212,3 +212,39 @@ def test_select_strategy_is_process_wide_and_returns_previous():
         assert L.tria_select_strategy(L.SELECT_AUTO) == L.SELECT_AUTO
     finally:
         L.tria_select_strategy(prev)
+
+
+def _calibrate(p=None, q=A, strides=(32 * 1024 * 128, 1024 * 128, 128), n_tokens=1024, ws=WS, ws_bytes=None,
+               outs=(A, A, A), r=None, mrl=None):
+    p = p or _params()
+    if ws_bytes is None:
+        ws_bytes = L.tria_calibrate_workspace_size(p, n_tokens)
+    L.tria_calibrate(p, q, *strides, n_tokens, *outs, r, mrl, ws, ws_bytes)
+
+
+def test_calibrate_workspace_size():
+    p = _params()
+    # [L][Hq][chunks of 1024 tokens][d/2][5] fp32 partial sums
+    assert L.tria_calibrate_workspace_size(p, 4096) == 2 * 32 * 4 * 64 * 5 * 4
+    assert L.tria_calibrate_workspace_size(p, 4097) == 2 * 32 * 5 * 64 * 5 * 4
+    assert L.tria_calibrate_workspace_size(p, 1) == 2 * 32 * 1 * 64 * 5 * 4
+    assert L.tria_calibrate_workspace_size(p, 0) == 0
+    assert L.tria_calibrate_workspace_size(_params(head_dim=96), 1024) == 0
+
+
+def test_calibrate_checks():
+    # every call below fails validation before any launch
+    assert _status(lambda: _calibrate(n_tokens=0, ws_bytes=1 << 30)) == L.TRIA_EINVAL
+    assert _status(lambda: _calibrate(q=None)) == L.TRIA_EINVAL
+    assert _status(lambda: _calibrate(outs=(A, None, A))) == L.TRIA_EINVAL
+    assert _status(lambda: _calibrate(q=A + 8)) == L.TRIA_ESHAPE
+    assert _status(lambda: _calibrate(strides=(8, 8, 12))) == L.TRIA_ESHAPE
+    assert _status(lambda: _calibrate(strides=(8, -8, 16))) == L.TRIA_ESHAPE
+    assert _status(lambda: _calibrate(ws=None)) == L.TRIA_EWORKSPACE
+    assert _status(lambda: _calibrate(ws=WS + 64)) == L.TRIA_EWORKSPACE
+    need = L.tria_calibrate_workspace_size(_params(), 1024)
+    assert _status(lambda: _calibrate(ws_bytes=need - 1)) == L.TRIA_EWORKSPACE
+    assert _status(lambda: _calibrate(p=_params(pairing=7), ws_bytes=1 << 30)) == L.TRIA_EINVAL
+    # more (layer, query head) pairs than one launch dimension holds
+    big = _params(n_layers=2100, n_kv_heads=8, group=4)
+    assert _status(lambda: _calibrate(p=big, ws_bytes=1 << 40)) == L.TRIA_ESHAPE
