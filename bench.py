@@ -90,12 +90,12 @@ def cpu_baseline(cfg, seconds: float) -> dict:
             "host_cpus": os.cpu_count()}
 
 
-def recorded_traffic(cfg_name: str):
-    """k_score's HBM bytes per launch from the committed rocprofv3 counter summary of
+def recorded_traffic(kernel: str, workload: str):
+    """A kernel's HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, if one exists and the kernel sources are the ones it measured;
     else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"k_score_{cfg_name}_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -255,7 +255,8 @@ def bench_calibrate(args) -> int:
         "algorithmic_bytes_per_step": alg,
         "kernel_ms": {"k_calib+k_calib_final": kms},
         "roofline": {"kernel": "k_calib (with k_calib_final)", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("k_calib", f"calibrate_{cfg.name}"),
                      "algorithmic_bytes_per_launch": alg},
         "cpu_baseline": base,
     }))
@@ -387,7 +388,7 @@ def main() -> int:
                           "ms_per_step_with_kernel_events": ms_inst},
         "roofline": {"kernel": "k_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(cfg.name),
+                     "traffic": recorded_traffic("k_score", cfg.name),
                      "algorithmic_bytes_per_launch": score_bytes, "dominant_kernel": dom},
         "cpu_baseline": base,
     }
