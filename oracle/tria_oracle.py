@@ -120,6 +120,21 @@ def s_trig_direct(mu: np.ndarray, k: np.ndarray, dist: np.ndarray, offsets, omeg
     return total / len(offsets)
 
 
+def s_trig_direct_max(mu: np.ndarray, k: np.ndarray, dist: np.ndarray, offsets, omega: np.ndarray) -> np.ndarray:
+    """The variant that takes the maximum over the future offsets instead of the
+    mean: max over delta in D of the band sum of Eq. 2 at distance Delta + delta.
+    Not linear in the offsets, so no fold applies; evaluated literally, offset by
+    offset.  [Fold note, sec. 4: the non-default maximum-over-offsets variant;
+    Eq. 2 for each term]"""
+    mag = np.abs(mu)[None, :] * np.abs(k)                       # [n][F]
+    phi = np.angle(mu)[None, :] - np.angle(k)                   # [n][F]
+    best = np.full(k.shape[0], -np.inf, dtype=np.float64)
+    for delta in list(offsets):
+        ang = np.outer(np.asarray(dist, np.float64) + float(delta), omega) + phi
+        best = np.maximum(best, np.sum(mag * np.cos(ang), axis=1))
+    return best
+
+
 def s_trig_phasor(mu: np.ndarray, k: np.ndarray, dist: np.ndarray, offsets, omega: np.ndarray) -> np.ndarray:
     """Same quantity via the phasor form Re sum_f E[q_f] conj(k_f) e^{i omega_f Delta}
     (Eq. 3), averaged over D (Eq. 4).  [Fold note, Eqs. 3 and 4]"""
@@ -183,18 +198,27 @@ S_TRIG_FORMS = {
 
 
 def score_head(rows: np.ndarray, pos: np.ndarray, q_pos: int, mu: np.ndarray, abs_mean: np.ndarray,
-               head_dim: int, pairing: str, theta: float, offsets, form: str = "folded") -> np.ndarray:
+               head_dim: int, pairing: str, theta: float, offsets, form: str = "folded",
+               reduce: str = "mean") -> np.ndarray:
     """S~(k) = (offset-averaged S_trig) + S_norm for every cached key of one KV head,
     seen by one q-head's calibrated centre.  [Fold note, Eqs. 1, 4, 6]
 
     ``rows`` [n][d] real post-rotation keys (fp64), ``pos`` [n] key positions,
     ``q_pos`` the current query position, ``mu`` [F] complex centre,
-    ``abs_mean`` [F] the calibrated E|q_f|.
+    ``abs_mean`` [F] the calibrated E|q_f|.  ``reduce="max"`` takes the maximum
+    over the offsets instead (the direct form only; S_norm does not depend on the
+    offset, so max_delta (S_trig + S_norm) = max_delta S_trig + S_norm).
     """
     omega = band_frequencies(head_dim, theta)
     k = invert_rope(complex_bands(rows, pairing), pos, omega)
     dist = float(q_pos) - np.asarray(pos, np.float64)
-    return S_TRIG_FORMS[form](mu, k, dist, offsets, omega) + s_norm(mu, abs_mean, k)
+    if reduce == "max":
+        trig = s_trig_direct_max(mu, k, dist, offsets, omega)
+    elif reduce == "mean":
+        trig = S_TRIG_FORMS[form](mu, k, dist, offsets, omega)
+    else:
+        raise ValueError(f"unknown offset reduction {reduce!r}")
+    return trig + s_norm(mu, abs_mean, k)
 
 
 # ----------------------------------------------------------------------------- selection
@@ -263,7 +287,7 @@ def compact(rows: np.ndarray, kept: np.ndarray) -> np.ndarray:
 
 def run_unit(k_bits: np.ndarray, pos: np.ndarray, q_pos: int, q_mean_re: np.ndarray, q_mean_im: np.ndarray,
              q_abs_mean: np.ndarray, *, head_dim: int, group: int, pairing: str, theta: float, offsets,
-             sink: int, window: int, agg: str, budget: int, form: str = "folded"):
+             sink: int, window: int, agg: str, budget: int, form: str = "folded", reduce: str = "mean"):
     """The whole pass for one unit (one layer of one sequence).
 
     ``k_bits`` [Hkv][n][d] bf16 bits of the cached keys, ``pos`` [n] or
@@ -279,7 +303,7 @@ def run_unit(k_bits: np.ndarray, pos: np.ndarray, q_pos: int, q_mean_re: np.ndar
         g = h // group
         p = pos if pos.ndim == 1 else pos[g]
         raw[h] = score_head(bf16_bits_to_f64(k_bits[g]), p, q_pos, mu[h], q_abs_mean[h],
-                            head_dim, pairing, theta, offsets, form)
+                            head_dim, pairing, theta, offsets, form, reduce)
     a = aggregate_unit(raw, n, group, sink, window, agg)
     kept = [select(a[g], budget) for g in range(Hkv)]
     return raw, a, kept

@@ -458,3 +458,64 @@ def test_calibration_feeds_the_norm_weight():
     q = _bits(np.round(rng.normal(size=(64, 16)) * 16) / 16 + 0.5)
     mre, mim, ab, r, _ = o.calibrate(q, "neox")
     np.testing.assert_allclose(ab * (1 - r), ab - np.abs(mre + 1j * mim), atol=1e-15)
+
+
+# --------------------------------------------------------------------------- maximum over offsets
+
+def test_max_over_offsets_one_band_hand_values():
+    """One band, omega_0 = 1, centre 1 and key 1 at distance 0: the offset-delta term
+    is cos(delta), so max over {1, 2} is cos 1 and max over {2, 3} is cos 2 (the less
+    negative), while the mean over {1, 2} is (cos 1 + cos 2) / 2."""
+    rows = np.array([[1.0, 0.0]])
+    mu = np.array([1.0 + 0j])
+    s = lambda offs, red: o.score_head(rows, np.array([0]), 0, mu, np.abs(mu), 2, "neox", 1e4, offs, "direct",
+                                       red)[0]
+    assert s([1, 2], "max") == pytest.approx(math.cos(1), abs=1e-15)
+    assert s([2, 3], "max") == pytest.approx(math.cos(2), abs=1e-15)
+    assert s([3, 2], "max") == pytest.approx(math.cos(2), abs=1e-15)
+    assert s([1, 2], "mean") == pytest.approx((math.cos(1) + math.cos(2)) / 2, abs=1e-15)
+
+
+@pytest.mark.parametrize("pairing", ["neox", "interleaved"])
+def test_max_over_offsets_is_the_max_of_single_offset_scores(pairing):
+    """max over D equals the maximum of |D| single-offset evaluations of the folded
+    form (an independent path: W_f of one offset is just its phasor), and is at least
+    the offset mean; a single offset gives max = mean."""
+    rng = np.random.default_rng(21)
+    d, theta, n = 32, 1e6, 40
+    F = d // 2
+    k_rows = rng.normal(size=(n, d))
+    pos = rng.permutation(100)[:n]
+    mu = rng.normal(size=F) + 1j * rng.normal(size=F)
+    absm = np.abs(mu) * (1.0 + rng.uniform(0, 0.5, size=F))
+    offsets = [2 ** i for i in range(12)] + [0, 7]
+    args = (k_rows, pos, 120, mu, absm, d, pairing, theta)
+    got = o.score_head(*args, offsets, "direct", "max")
+    each = np.stack([o.score_head(*args, [dl], "folded") for dl in offsets])
+    np.testing.assert_allclose(got, each.max(axis=0), rtol=0, atol=1e-10)
+    assert np.all(got >= o.score_head(*args, offsets, "direct") - 1e-12)
+    one = o.score_head(*args, [5], "direct", "max")
+    np.testing.assert_allclose(one, o.score_head(*args, [5], "folded"), rtol=0, atol=1e-10)
+    # duplicates and order do not matter
+    np.testing.assert_array_equal(got, o.score_head(*args, offsets[::-1] + offsets[:3], "direct", "max"))
+
+
+@pytest.mark.parametrize("pairing", ["neox", "interleaved"])
+def test_max_over_offsets_is_the_max_rotary_logit(pairing):
+    """With no norm term, the maximum over D is max_delta <RoPE(q, p_q + delta),
+    RoPE(k, p_k)>, the rotary logit of a query moved delta positions ahead,
+    computed with HF transformers' RoPE."""
+    rng = np.random.default_rng(23)
+    d, theta = 64, 1e4
+    n = 30
+    k_pre = rng.normal(size=(n, d))
+    q_vec = rng.normal(size=(1, d))
+    pos = rng.integers(0, 40, size=n)
+    q_pos = 45
+    offsets = [1, 2, 4, 8, 16, 3]
+    rope = (lambda x, p: _llama_rope(x, p, d, theta)) if pairing == "neox" else (lambda x, p: _gptj_rope(x, p, d))
+    k_rot = rope(k_pre, pos)
+    logits = np.stack([k_rot @ rope(q_vec, np.array([q_pos + dl]))[0] for dl in offsets])
+    mu = o.complex_bands(q_vec[0], pairing)
+    got = o.score_head(k_rot, pos, q_pos, mu, np.abs(mu), d, pairing, theta, offsets, "direct", "max")
+    np.testing.assert_allclose(got, logits.max(axis=0), atol=1e-4 * np.max(np.abs(logits)))
