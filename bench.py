@@ -31,7 +31,7 @@ def workload_desc(cfg) -> dict:
     d = {"workload": cfg.name, "layers": cfg.n_layers, "sequences": cfg.n_seqs, "kv_heads": cfg.n_kv_heads,
          "q_heads": cfg.n_q_heads, "head_dim": cfg.head_dim, "n_kv": cfg.n_kv, "pairing": cfg.pairing,
          "rope_base": cfg.rope_base, "offsets": len(cfg.offsets), "window": cfg.window, "sink": cfg.sink,
-         "gqa": cfg.agg, "paged": cfg.paged}
+         "gqa": cfg.agg, "paged": cfg.paged, "offset_reduce": cfg.offset_reduce}
     if cfg.budget_frac:
         d["budget"] = f"{cfg.budget_frac:g} of each length"
     else:
@@ -70,7 +70,8 @@ def cpu_baseline(cfg, seconds: float) -> dict:
                 t0 = time.perf_counter()
                 rows = o.bf16_bits_to_f64(k_bits)
                 raw = np.stack([o.score_head(rows, pos, int(u.q_pos[unit]), mu[layer, h], absm[layer, h],
-                                             cfg.head_dim, cfg.pairing, cfg.rope_base, cfg.offsets, "folded")
+                                             cfg.head_dim, cfg.pairing, cfg.rope_base, cfg.offsets, "folded",
+                                             cfg.offset_reduce)
                                 for h in range(g * G, (g + 1) * G)])
                 agg = o.aggregate_unit(raw, n, G, cfg.sink, cfg.window, cfg.agg)[0]
                 kept = o.select(agg, int(u.budget[unit]))
@@ -85,7 +86,8 @@ def cpu_baseline(cfg, seconds: float) -> dict:
             if spent >= seconds:
                 break
     return {"value": keys / spent / 1e6, "unit": "M keys/s", "cores": 1, "kind": "oracle",
-            "sample": f"{pairs} (unit, KV head) pairs = {keys} keys of {cfg.name}, fp64 folded form, "
+            "sample": f"{pairs} (unit, KV head) pairs = {keys} keys of {cfg.name}, fp64 "
+                      f"{'direct form, maximum over offsets' if cfg.offset_reduce == 'max' else 'folded form'}, "
                       f"{spent:.1f} s on one host thread",
             "host_cpus": os.cpu_count()}
 
@@ -279,6 +281,8 @@ def main() -> int:
                     help="instead of the pass, time the calibration reduction (tria_calibrate) over a "
                          "synthetic pre-RoPE query stream of --tokens rows per (layer, query head)")
     ap.add_argument("--tokens", type=int, default=8192, help="calibration tokens (with --calibrate)")
+    ap.add_argument("--offsets", choices=("mean", "max"), default="mean",
+                    help="reduction over the future offsets: the mean (the method) or the maximum variant")
     args = ap.parse_args()
     # a calibration step is ~0.4 ms: more of them keep the timed region near 0.1 s
     if args.steps is None:
@@ -300,6 +304,9 @@ def main() -> int:
     from key_importance_scoring_amd.device import DeviceProblem
 
     cfg = synth.CONFIGS[args.config]
+    cache_name = cfg.name          # the offset reduction does not change the inputs
+    if args.offsets == "max":
+        cfg = cfg.replace(name=f"{cfg.name}_offsets_max", offset_reduce="max")
     print(f"[bench] building {cfg.name} inputs", file=sys.stderr, flush=True)
     hosts = {}
     if args.input_cache:
@@ -307,7 +314,7 @@ def main() -> int:
         from key_importance_scoring_amd.device import host_cache
         os.makedirs(args.input_cache, exist_ok=True)
         for which in ("k", "v"):
-            path = os.path.join(args.input_cache, f"{cfg.name}_s{cfg.seed}_{which}.npy")
+            path = os.path.join(args.input_cache, f"{cache_name}_s{cfg.seed}_{which}.npy")
             if os.path.exists(path):
                 hosts[which] = np.load(path, mmap_mode="r")
             else:
@@ -354,6 +361,10 @@ def main() -> int:
     dom = max(per_kernel, key=per_kernel.get)
     # algorithmic bytes of k_score per launch: every cached K row read once
     score_bytes = keys * 2 * cfg.head_dim
+    # its useful MFMA work: per (key, query head) a d-long dot product per offset
+    # (maximum variant) or one folded dot product (the mean), plus the norm term's d/2
+    dots = len(cfg.offsets) if cfg.offset_reduce == "max" else 1
+    score_flops = keys * cfg.group * 2 * (cfg.head_dim * dots + cfg.head_dim // 2)
     score_ms = per_kernel["k_score"]
     achieved = score_bytes / (score_ms / 1e3) / 1e9
     print(f"[bench] {ms:.3f} ms/step ({ms_inst:.3f} with per-kernel events), wall {wall / args.steps * 1e3:.3f} "
@@ -389,7 +400,9 @@ def main() -> int:
         "roofline": {"kernel": "k_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic("k_score", cfg.name),
-                     "algorithmic_bytes_per_launch": score_bytes, "dominant_kernel": dom},
+                     "algorithmic_bytes_per_launch": score_bytes, "dominant_kernel": dom,
+                     "mfma_bf16_tflops": score_flops / (score_ms / 1e3) / 1e12,
+                     "mfma_frac_of_bf16_dense_peak": score_flops / (score_ms / 1e3) / 2.5e15},
         "cpu_baseline": base,
     }
     print(json.dumps(out))

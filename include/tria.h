@@ -70,6 +70,12 @@ typedef enum { TRIA_PAIR_NEOX = 0, TRIA_PAIR_INTERLEAVED = 1 } tria_pairing;
  * "normalize-then-max"; the mean is the other variant].                        */
 typedef enum { TRIA_AGG_MEAN = 0, TRIA_AGG_MAX = 1 } tria_agg;
 
+/* How the score reduces over the future offsets D: the mean (the method,
+ * [Fold note, Eq. 4], folded exactly into one weight per band, Eqs. 5-7) or the
+ * maximum (the non-default variant [Fold note, sec. 4]; no fold applies, each
+ * offset is scored on its own and the largest taken).                         */
+typedef enum { TRIA_OFFSETS_MEAN = 0, TRIA_OFFSETS_MAX = 1 } tria_offset_reduce;
+
 /* Device-side contract violations, OR-ed into the workspace flag word.        */
 enum {
   TRIA_FLAG_LEN = 1,     /* len[u] < 0 or > n_max: clamped                     */
@@ -96,10 +102,12 @@ typedef struct tria_params {
   double rope_base;        /* theta > 1: band f turns at theta^(-2f/d) rad per
                               position [Fold note, Eq. 2]                       */
   const int64_t* offsets;  /* [host] future offsets D, each in [0, 2^40]; the
-                              score is averaged over them [Fold note, Eq. 4]    */
+                              score is reduced over them (offset_reduce)        */
   int32_t n_offsets;       /* |D|, 1..256                                       */
   int32_t sink;            /* S0 >= 0: the first S0 slots are always kept       */
   int32_t window;          /* W >= 0: the last W slots are always kept          */
+  int32_t offset_reduce;   /* tria_offset_reduce; 0 (the mean) for a struct
+                              that is zero-initialised                          */
 } tria_params;
 
 /* A K or V cache.  Row of (unit u, KV head g, slot i) starts at element
@@ -142,7 +150,14 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max)
  * [Fold note, Eqs. 1, 2, 4; the norm term is the reading E|q_f| (1 - R_f) |k_f|
  * of Blog, The Method].  The kernels evaluate it in the folded form of Eq. 7
  * with the inverse rotation absorbed by angle addition, so key positions are
- * not needed: only q_pos.
+ * not needed: only q_pos.  With p->offset_reduce = TRIA_OFFSETS_MAX the mean
+ * over D is replaced by the maximum over D [Fold note, sec. 4]: each offset's
+ * band sum is one dot product of the key row with the coefficients
+ * mu_f e^{i omega_f (q_pos + delta)}, evaluated for every delta.  That mode
+ * stages every offset's coefficients in LDS and returns TRIA_ESHAPE when they
+ * do not fit (ceil(|D| G' / 8) * d / 32 KiB, G' = G rounded up to a power of two,
+ * beside the score tiles; 17 offsets fit for every head_dim and group except
+ * d = 256 with G > 4).
  * Then, over the droppable slots C = [sink, n - window) (the candidates):
  *   z_h(i)     = (raw[u][h][i] - mean_C) / max(std_C, 1e-12)   (population std)
  *   agg[u][g][i] = mean_h z_h(i)  or  max_h z_h(i)   (per p->agg)

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtria.so"
 TRIA_OK, TRIA_EINVAL, TRIA_ESHAPE, TRIA_EBUDGET, TRIA_EOVERLAP, TRIA_EWORKSPACE, TRIA_ELAUNCH = range(7)
 PAIR_NEOX, PAIR_INTERLEAVED = 0, 1
 AGG_MEAN, AGG_MAX = 0, 1
+OFFSETS_MEAN, OFFSETS_MAX = 0, 1
 FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
@@ -35,7 +36,8 @@ class TriaError(RuntimeError):
 class TriaParams(ctypes.Structure):
     _fields_ = [("head_dim", c_int32), ("n_kv_heads", c_int32), ("group", c_int32), ("n_layers", c_int32),
                 ("pairing", c_int32), ("agg", c_int32), ("rope_base", c_double),
-                ("offsets", POINTER(c_int64)), ("n_offsets", c_int32), ("sink", c_int32), ("window", c_int32)]
+                ("offsets", POINTER(c_int64)), ("n_offsets", c_int32), ("sink", c_int32), ("window", c_int32),
+                ("offset_reduce", c_int32)]
 
 
 class TriaKvView(ctypes.Structure):
@@ -119,11 +121,11 @@ def stream_handle(stream) -> int | None:
 
 
 def make_params(head_dim: int, n_kv_heads: int, group: int, n_layers: int, pairing: int, agg: int,
-                rope_base: float, offsets, sink: int, window: int) -> TriaParams:
+                rope_base: float, offsets, sink: int, window: int, offset_reduce: int = OFFSETS_MEAN) -> TriaParams:
     """A TriaParams; the offsets array is kept alive on the returned object."""
     arr = (c_int64 * len(offsets))(*[int(o) for o in offsets])
     p = TriaParams(head_dim, n_kv_heads, group, n_layers, pairing, agg, float(rope_base),
-                   ctypes.cast(arr, POINTER(c_int64)), len(offsets), sink, window)
+                   ctypes.cast(arr, POINTER(c_int64)), len(offsets), sink, window, offset_reduce)
     p._offsets_keepalive = arr
     return p
 

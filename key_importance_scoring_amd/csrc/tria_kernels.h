@@ -17,7 +17,8 @@ constexpr int kScoreTileMax = 2048;
 #ifndef TRIA_SCORE_TILE_SMALL_G
 #define TRIA_SCORE_TILE_SMALL_G 2048
 #endif
-inline int score_tile_keys(int group) { return group <= 4 ? TRIA_SCORE_TILE_SMALL_G : 1024; }
+// (the maximum over offsets stages its coefficient blocks beside the tiles: 1024)
+inline int score_tile_keys(int group, int omax = 0) { return group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : 1024; }
 // A tile's published moments start as this bit pattern (cleared by k_coef): a NaN
 // whose low payload bits are set, which no moment computed from fp32 scores can
 // take (NaNs that arithmetic produces keep an fp32 payload or are the default one).
@@ -28,6 +29,24 @@ constexpr int kPollLimit = 1 << 16;
 // Linear bins of an aggregate (a z-score: scale-free): 2048 bins over [-8, 8), one
 // below, one above, one for +inf (protected slots).
 constexpr int kBins = 2052;
+
+// Coefficient blocks of the maximum-over-offsets mode (16 MFMA B columns each:
+// hi parts in columns 0..7, lo parts in 8..15).  With G' = G rounded up to a power
+// of two, a block holds opb = 8 / G' offsets: column q G' + h is query head h at the
+// block's q-th offset (offsets in order, the last block padded by repeating the
+// last offset, which leaves the maximum unchanged; columns of heads >= G are zero).
+struct OffsetBlocks {
+  int gp;       // G': column stride of one offset
+  int opb;      // offsets per block
+  int nblk;     // blocks per (unit, KV head)
+};
+__host__ __device__ inline OffsetBlocks offset_blocks(int n_offsets, int group) {
+  OffsetBlocks ob;
+  ob.gp = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
+  ob.opb = 8 / ob.gp;
+  ob.nblk = (n_offsets + ob.opb - 1) / ob.opb;
+  return ob;
+}
 
 // A cache view with element strides (bf16 elements).
 struct KView {
@@ -67,6 +86,9 @@ struct CoefArgs {
   int32_t* next_tile;         // tile claim counter of k_score, cleared here
   uint32_t* hist;             // [U][Hkv][kBins] aggregate histograms of k_score, cleared here
   int32_t* flags;
+  int32_t omax;               // 1: maximum over the offsets
+  uint32_t* Bmax;             // omax: [U][Hkv][nblk][d/32][64] 16-byte B operands of the offset blocks
+  OffsetBlocks ob;
 };
 
 struct ScoreArgs {
@@ -80,6 +102,9 @@ struct ScoreArgs {
   int32_t* next_tile;         // next tile to claim
   uint32_t* hist;             // [U][Hkv][kBins] histogram of the aggregates' linear bins
   int32_t* flags;
+  int32_t omax;               // 1: maximum over the offsets (B operands of the norm part still in B)
+  const uint32_t* Bmax;       // omax: [U][Hkv][nblk][d/32][64] 16-byte B operands of the offset blocks
+  OffsetBlocks ob;
 };
 
 // Per-(unit, KV head) state of the selection, in the workspace.
@@ -155,7 +180,9 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s);
 // Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
 // of one (unit, KV head) must be resident together for the moment exchange.
-int score_capacity(int d, int pairing, bool paged, int group);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk);
+// LDS bytes of one k_score workgroup
+size_t score_lds(int d, int group, bool paged, int omax, int nblk);
 // strategy: 0 automatic, 1 per group (when n_max fits), 2 tiled
 hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);

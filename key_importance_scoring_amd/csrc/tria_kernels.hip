@@ -161,6 +161,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   __shared__ double rot_re[F], rot_im[F];
   __shared__ float s_c[kMaxGroup * D];  // coefficient rows, pairing layout
   __shared__ float s_n[kMaxGroup * F];  // norm weights
+  __shared__ double s_mur[kMaxGroup * F], s_mui[kMaxGroup * F], s_w[F];  // maximum over offsets
 
   // tiles past len[u] hold no keys: their moments are published here, as zeros
   const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
@@ -231,7 +232,12 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     s_c[h * D + (P == 0 ? b + F : 2 * b + 1)] = (float)ci;
     // norm weight E|q_f| - |E q_f| = E|q_f| (1 - R_f)  [Blog, The Method; reading]
     s_n[h * F + b] = (float)(ab[k] - sqrt(mr[k] * mr[k] + mi[k] * mi[k]));
+    if (a.omax) {
+      s_mur[h * F + b] = mr[k];
+      s_mui[h * F + b] = mi[k];
+    }
   }
+  if (a.omax && t < F) s_w[t] = w;
   __syncthreads();
 
   // B operands: operand s of lane l at B[(u, g)][s][l]; s < NKC are the dot part's
@@ -268,6 +274,51 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
       }
     }
     dst[s * 64 + lane] = w4;
+  }
+
+  // maximum over offsets: one coefficient row per (query head, offset),
+  // c = E[q_f] e^{i w_f (q_pos + delta)}, nothing averaged [Fold note, sec. 4; Eq. 3
+  // per offset], written as the offset blocks' B operands: column j = q G' + h < 8
+  // of block cb is the hi part of head h at offset cb opb + q, column 8 + j the lo
+  // part.  The angle is reduced modulo 2 pi in fp64 before an fp32 sine and cosine
+  // (the operands keep ~16 bits).
+  if (a.omax) {
+    const OffsetBlocks ob = a.ob;
+    const double qp = (double)a.q_pos[u];
+    u32x4* dstm = reinterpret_cast<u32x4*>(a.Bmax) + ug * ob.nblk * S::NKC * 64;
+    const int nq = ob.nblk * S::NKC * 64;
+    for (int q = t; q < nq; q += 256) {
+      const int cb = q / (S::NKC * 64), i = (q / 64) % S::NKC, lane = q % 64;
+      const int col = lane & 15, grp = lane >> 4, j = col & 7;
+      const bool lo = col >= 8;
+      const int head = j % ob.gp < G ? j % ob.gp : -1;
+      const int oi = min(cb * ob.opb + j / ob.gp, offs.n - 1);
+      u32x4 w4 = {0u, 0u, 0u, 0u};
+      if (head >= 0) {
+        const double x = qp + offs.v[oi];
+        const int e0 = chunk_elem<D>(i, grp);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int el = e0 + e;
+          const int bnd = P == 0 ? (el < F ? el : el - F) : el / 2;
+          const bool im = P == 0 ? el >= F : (el & 1);
+          const double ang = s_w[bnd] * x;
+          const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
+          float sv, cv;
+          sincosf(r, &sv, &cv);
+          const double mr = s_mur[head * F + bnd], mi = s_mui[head * F + bnd];
+          v[e] = (float)(im ? mr * (double)sv + mi * (double)cv : mr * (double)cv - mi * (double)sv);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          uint32_t hi, lw;
+          split_bf16(v[2 * jj], v[2 * jj + 1], hi, lw);
+          w4[jj] = lo ? lw : hi;
+        }
+      }
+      dstm[q] = w4;
+    }
   }
 }
 
@@ -318,9 +369,12 @@ __device__ inline float band_sq(const u32x4 (&ch)[D / 32], int q) {
 #define TRIA_SCORE_NBI 4
 #endif
 
-// 16-key blocks per pipeline stage (d = 256 rows are twice as large: half as many)
-template <int D>
-constexpr int stage_blocks() { return D >= 256 ? (TRIA_SCORE_NBI + 1) / 2 : TRIA_SCORE_NBI; }
+// 16-key blocks per pipeline stage (d = 256 rows are twice as large: half as many;
+// the maximum over offsets keeps more accumulators: half as many again)
+template <int D, bool MAXO = false>
+constexpr int stage_blocks() {
+  return MAXO ? (D >= 256 ? 2 : 4) : (D >= 256 ? (TRIA_SCORE_NBI + 1) / 2 : TRIA_SCORE_NBI);
+}
 // a wave's keys (tile / 4, tiles of 1024 or 2048) must be whole stages: a stage's
 // scores are written to LDS for all its keys, and a partial last stage would write
 // into the next wave's range
@@ -328,18 +382,18 @@ static_assert((1024 / 4) % (16 * stage_blocks<64>()) == 0 && (1024 / 4) % (16 * 
               "stage size must divide a wave's keys");
 
 // One pipeline stage of a wave: stage_blocks blocks of 16 keys, d/32 16-byte chunks per lane each.
-template <int D>
-using Stage = u32x4[stage_blocks<D>()][D / 32];
+template <int D, bool MAXO = false>
+using Stage = u32x4[stage_blocks<D, MAXO>()][D / 32];
 
 // Issues the loads of one stage.  Keys at or past `kend` (the end of the wave's
 // range) are clamped to its last key, whose row is already in cache: their scores
 // are computed but never counted.  Every load is unconditional, so the
 // compiler can keep the next stage in flight while the current one computes.
-template <int D, bool PAGED>
-__device__ inline void load_stage(Stage<D>& ch, const KView& k, int u, int g, int kb, int kend, int col, int grp,
-                                  const int* s_bt, int page0) {
+template <int D, bool PAGED, bool MAXO = false>
+__device__ inline void load_stage(Stage<D, MAXO>& ch, const KView& k, int u, int g, int kb, int kend, int col,
+                                  int grp, const int* s_bt, int page0) {
 #pragma unroll
-  for (int b = 0; b < stage_blocks<D>(); ++b) {
+  for (int b = 0; b < stage_blocks<D, MAXO>(); ++b) {
     const int key = min(kb + 16 * b + col, kend - 1);
     const uint16_t* rp;
     if (!PAGED) {
@@ -379,10 +433,11 @@ __device__ inline void tile_len(const ScoreArgs& a, TileInfo& ti, int n_loaded, 
 
 // Scores one tile into LDS (s_raw, [G][tile + 16]), writes the per-query-head
 // scores if wanted, and publishes the tile's candidate moments.
-template <int D, int P, bool PAGED>
-__device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known, float* s_raw, int* s_bt) {
+template <int D, int P, bool PAGED, bool MAXO>
+__device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known, float* s_raw, int* s_bt,
+                                   u32x4* s_bmax, int* s_bug) {
   using S = Shape<D>;
-  constexpr int NBI = stage_blocks<D>();
+  constexpr int NBI = stage_blocks<D, MAXO>();
   constexpr int STAGE = 16 * NBI;  // keys per pipeline stage
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -427,8 +482,33 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
 
   // the first stage, unconditionally and possibly before len[u] is known: a wave with
   // no keys reloads row kcap - 1, which is below n_max and at or past tile0
-  Stage<D> cA, cB;
-  load_stage<D, PAGED>(cA, a.k, u, g, kw0, kcap, col, grp, s_bt, page0);
+  Stage<D, MAXO> cA, cB;
+  load_stage<D, PAGED, MAXO>(cA, a.k, u, g, kw0, kcap, col, grp, s_bt, page0);
+
+  // maximum over offsets: the (unit, KV head)'s offset blocks into LDS, unless the
+  // previous tile of this workgroup already staged them (its reads have ended at the
+  // barrier that closed its score loop)
+  if constexpr (MAXO) {
+    if (*s_bug != ti.ug) {
+      const int nq = a.ob.nblk * S::NKC * 64;
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.Bmax) + (size_t)ti.ug * nq;
+      for (int q0 = 0; q0 < nq; q0 += 256 * 8) {
+        u32x4 tmp[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int q = min(q0 + (int)threadIdx.x + 256 * k, nq - 1);
+          tmp[k] = src[q];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int q = q0 + (int)threadIdx.x + 256 * k;
+          if (q < nq) s_bmax[q] = tmp[k];
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) *s_bug = ti.ug;
+    }
+  }
 
   tile_len(a, ti, n_loaded, true);
   const int n = ti.n;
@@ -447,7 +527,7 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
 
   // scores of one loaded stage: dot-product MFMAs of every block first (independent
   // accumulators), then per block the magnitudes and the norm-term MFMAs
-  auto compute = [&](const Stage<D>& ch, int kb) {
+  auto compute = [&](const Stage<D, MAXO>& ch, int kb) {
     f32x4 acc[NBI];
 #pragma unroll
     for (int b = 0; b < NBI; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -488,17 +568,103 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     }
   };
 
+  // maximum over offsets: per stage, the norm term once, then every offset block
+  // (MFMA; hi + lo merged into lanes 8..15; in-lane running maximum), then the
+  // offsets a row's lanes hold meet in the owner lane 8 + h of each query head
+  auto compute_max = [&](const Stage<D, MAXO>& ch, int kb) {
+    f32x4 nrm[NBI], best[NBI];
+#pragma unroll
+    for (int b = 0; b < NBI; ++b) {
+      nrm[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < S::NNC; ++i) {
+        u32x4 h4, l4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float m0 = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch[b], 8 * i + 2 * j));
+          const float m1 = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch[b], 8 * i + 2 * j + 1));
+          uint32_t hi, lw;
+          split_bf16(m0, m1, hi, lw);
+          h4[j] = hi;
+          l4[j] = lw;
+        }
+        nrm[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h4), bna[i], nrm[b], 0, 0, 0);
+        nrm[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l4), bnb[i], nrm[b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) best[b][t] = -__builtin_inff();
+    }
+    // blocks in order, the next block's B operands read from LDS while the current
+    // block's MFMAs run; lane 8 + q G' + h keeps the running maximum of head h over
+    // the offsets it holds (the q-th of every block)
+    const int nblk = a.ob.nblk;
+    bf16x8 bcur[S::NKC], bnext[S::NKC];
+#pragma unroll
+    for (int i = 0; i < S::NKC; ++i) bcur[i] = __builtin_bit_cast(bf16x8, s_bmax[i * 64 + lane]);
+    for (int cb = 0; cb < nblk; ++cb) {
+      const int cn = min(cb + 1, nblk - 1);
+#pragma unroll
+      for (int i = 0; i < S::NKC; ++i) bnext[i] = __builtin_bit_cast(bf16x8, s_bmax[(cn * S::NKC + i) * 64 + lane]);
+      f32x4 acc[NBI];
+#pragma unroll
+      for (int b = 0; b < NBI; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < S::NKC; ++i)
+#pragma unroll
+        for (int b = 0; b < NBI; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[b][i]), bcur[i], acc[b], 0,
+                                                           0, 0);
+#pragma unroll
+      for (int b = 0; b < NBI; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[b][t]), 0x118, 0xF, 0xF, true);
+          best[b][t] = fmaxf(best[b][t], acc[b][t] + __int_as_float(other));
+        }
+#pragma unroll
+      for (int i = 0; i < S::NKC; ++i) bcur[i] = bnext[i];
+    }
+    // the offsets held by lanes 8 + q G' + h, q < opb, meet in lane 8 + h: row shifts
+    // by G', 2 G', 4 G' (lane l takes lane l + s; lanes past the row are not used)
+    for (int sft = a.ob.gp; sft < 8; sft *= 2) {
+#pragma unroll
+      for (int b = 0; b < NBI; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int x = __float_as_int(best[b][t]);
+          const int y = sft == 1 ? __builtin_amdgcn_mov_dpp(x, 0x101, 0xF, 0xF, true)
+                      : sft == 2 ? __builtin_amdgcn_mov_dpp(x, 0x102, 0xF, 0xF, true)
+                                 : __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);
+          best[b][t] = fmaxf(best[b][t], __int_as_float(y));
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NBI; ++b) {
+      f32x4 sc;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(nrm[b][t]), 0x118, 0xF, 0xF, true);
+        sc[t] = best[b][t] + nrm[b][t] + __int_as_float(other);
+      }
+      if (owner) *reinterpret_cast<f32x4*>(s_row + kb + 16 * b + 4 * grp) = sc;
+    }
+  };
+
   // ---- register double buffer over the wave's keys [kw0, kend): the next stage's
   // loads are issued while the current stage computes.  (Keeping two stages in
   // flight across each wait measured slower on the full cache: more outstanding
   // requests per wave did not raise the delivered bandwidth.)
+  auto compute_stage = [&](const Stage<D, MAXO>& ch, int kb) {
+    if constexpr (MAXO) compute_max(ch, kb);
+    else compute(ch, kb);
+  };
   if (kw0 < kend) {
     for (int kb = kw0;; kb += 2 * STAGE) {
-      load_stage<D, PAGED>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
-      compute(cA, kb);
+      load_stage<D, PAGED, MAXO>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
+      compute_stage(cA, kb);
       if (kb + STAGE >= kend) break;
-      load_stage<D, PAGED>(cA, a.k, u, g, kb + 2 * STAGE, kend, col, grp, s_bt, page0);
-      compute(cB, kb + STAGE);
+      load_stage<D, PAGED, MAXO>(cA, a.k, u, g, kb + 2 * STAGE, kend, col, grp, s_bt, page0);
+      compute_stage(cB, kb + STAGE);
       if (kb + 2 * STAGE >= kend) break;
     }
   }
@@ -682,18 +848,26 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
 // wait; with P workgroups each holding at most two tiles, a circular wait would
 // need 2P <= n_tiles, and P >= n_tiles (the host checks it), so the wait always ends
 // (it is also bounded, and flagged, as a last resort).
-template <int D, int P, bool PAGED>
-__global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
+template <int D, int P, bool PAGED, bool MAXO>
+__device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
   extern __shared__ float s_dyn[];
   __shared__ int s_t;
+  __shared__ int s_bug;   // maximum over offsets: the (unit, KV head) whose offset blocks are staged
   const int G = a.group;
   const int RS = a.tile + 16;
   float* buf0 = s_dyn;
   float* buf1 = s_dyn + G * RS;
   int* s_bt = reinterpret_cast<int*>(s_dyn + 2 * G * RS);
-  const int scratch = PAGED && a.tile + 1 > kBins ? a.tile + 1 : kBins;
+  // the mean: one region for the tile's block ids (paged) and the finalisation's
+  // histogram; the maximum over offsets: the block ids only, the histogram shares
+  // the staged offset blocks' region (restaged after every finalisation)
+  const int scratch = MAXO ? (PAGED ? a.tile + 1 : 0) : (PAGED && a.tile + 1 > kBins ? a.tile + 1 : kBins);
   int* s_len = s_bt + scratch;            // [kListUnits] lengths
   int* s_pre = s_len + kListUnits;        // [kListUnits + 1] tiles of the units before
+  // maximum over offsets: the staged offset blocks, 16-byte aligned
+  u32x4* s_bmax = reinterpret_cast<u32x4*>(s_dyn + ((2 * G * RS + scratch + 2 * kListUnits + 1 + 3) & ~3));
+  uint32_t* s_hist = MAXO ? reinterpret_cast<uint32_t*>(s_bmax) : reinterpret_cast<uint32_t*>(s_bt);
+  if (threadIdx.x == 0) s_bug = -1;
   const int U = a.n_units;
   const bool listed = U <= kListUnits;
   int total = U * a.hkv * a.n_tiles;
@@ -752,17 +926,32 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
     int ug = 0, tile = 0;
     if (t < total) {
       place(t, ug, tile);
-      score_phase<D, P, PAGED>(a, tile_info(a, ug, tile), listed ? s_len[ug / a.hkv] : -1, b ? buf1 : buf0, s_bt);
+      score_phase<D, P, PAGED, MAXO>(a, tile_info(a, ug, tile), listed ? s_len[ug / a.hkv] : -1, b ? buf1 : buf0,
+                                     s_bt, s_bmax, &s_bug);
     }
-    // s_bt served the current tile's score phase; finalize reuses it as histogram scratch
-    if (pug >= 0)
-      finalize_tile(a, tile_info(a, pug, ptile), listed ? s_len[pug / a.hkv] : -1, b ? buf0 : buf1,
-                    reinterpret_cast<uint32_t*>(s_bt));
+    // s_bt (or, for the maximum over offsets, the offset blocks) served the current
+    // tile's score phase; finalize reuses it as histogram scratch
+    if (pug >= 0) {
+      finalize_tile(a, tile_info(a, pug, ptile), listed ? s_len[pug / a.hkv] : -1, b ? buf0 : buf1, s_hist);
+      if (MAXO && threadIdx.x == 0) s_bug = -1;
+    }
     if (t >= total) break;
     pug = ug;
     ptile = tile;
     b = !b;
   }
+}
+
+template <int D, int P, bool PAGED>
+__global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
+  score_kernel<D, P, PAGED, false>(a);
+}
+
+// The maximum over offsets: two workgroups per CU when LDS allows (G <= 4), so at
+// most 256 registers a lane.
+template <int D, int P, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_max(ScoreArgs a) {
+  score_kernel<D, P, PAGED, true>(a);
 }
 
 // ============================================================================ selection
@@ -1527,34 +1716,46 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-size_t score_lds(int group, bool paged) {
-  const int tile = score_tile_keys(group);
+size_t score_lds(int d, int group, bool paged, int omax, int nblk) {
+  const int tile = score_tile_keys(group, omax);
   // two score buffers, a region that holds the tile's block ids during the score
-  // phase and the aggregate histogram during finalisation, and the units' lengths and
-  // tile prefix
-  const size_t scratch = paged && tile + 1 > kBins ? (size_t)tile + 1 : (size_t)kBins;
-  return (size_t)2 * group * (tile + 16) * 4 + scratch * 4 + (size_t)(2 * kListUnits + 1) * 4;
+  // phase and (the mean) the aggregate histogram during finalisation, the units'
+  // lengths and tile prefix, and for the maximum over offsets the staged offset
+  // blocks, which share their region with the histogram
+  if (!omax) {
+    const size_t scratch = paged && tile + 1 > kBins ? (size_t)tile + 1 : (size_t)kBins;
+    return ((size_t)2 * group * (tile + 16) + scratch + (size_t)(2 * kListUnits + 1)) * 4;
+  }
+  const size_t scratch = paged ? (size_t)tile + 1 : 0;
+  const size_t base = (size_t)2 * group * (tile + 16) + scratch + (size_t)(2 * kListUnits + 1);
+  const size_t blocks = (size_t)nblk * (d / 32) * 64 * 16;
+  return ((base + 3) & ~(size_t)3) * 4 + (blocks > (size_t)kBins * 4 ? blocks : (size_t)kBins * 4);
 }
 
-int score_capacity(int d, int pairing, bool paged, int group) {
-  const size_t lds = score_lds(group, paged);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk) {
+  const size_t lds = score_lds(d, group, paged, omax, nblk);
   int per_cu = 0, dev = 0, cus = 0;
   hipError_t e = hipErrorInvalidValue;
-#define TRIA_OCC_CASE(DD, PP, PG)                                                                       \
-  if (d == DD && pairing == PP && paged == PG)                                                          \
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_score<DD, PP, PG>, 256, lds);
-  TRIA_OCC_CASE(64, 0, false)
-  TRIA_OCC_CASE(64, 1, false)
-  TRIA_OCC_CASE(128, 0, false)
-  TRIA_OCC_CASE(128, 1, false)
-  TRIA_OCC_CASE(256, 0, false)
-  TRIA_OCC_CASE(256, 1, false)
-  TRIA_OCC_CASE(64, 0, true)
-  TRIA_OCC_CASE(64, 1, true)
-  TRIA_OCC_CASE(128, 0, true)
-  TRIA_OCC_CASE(128, 1, true)
-  TRIA_OCC_CASE(256, 0, true)
-  TRIA_OCC_CASE(256, 1, true)
+#define TRIA_OCC_CASE(DD, PP, PG, MX)                                                                     \
+  if (d == DD && pairing == PP && paged == PG && (omax != 0) == MX)                                       \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                     \
+        &per_cu, MX ? (const void*)k_score_max<DD, PP, PG> : (const void*)k_score<DD, PP, PG>, 256, lds);
+#define TRIA_OCC_CASES(MX)        \
+  TRIA_OCC_CASE(64, 0, false, MX)  \
+  TRIA_OCC_CASE(64, 1, false, MX)  \
+  TRIA_OCC_CASE(128, 0, false, MX) \
+  TRIA_OCC_CASE(128, 1, false, MX) \
+  TRIA_OCC_CASE(256, 0, false, MX) \
+  TRIA_OCC_CASE(256, 1, false, MX) \
+  TRIA_OCC_CASE(64, 0, true, MX)   \
+  TRIA_OCC_CASE(64, 1, true, MX)   \
+  TRIA_OCC_CASE(128, 0, true, MX)  \
+  TRIA_OCC_CASE(128, 1, true, MX)  \
+  TRIA_OCC_CASE(256, 0, true, MX)  \
+  TRIA_OCC_CASE(256, 1, true, MX)
+  TRIA_OCC_CASES(false)
+  TRIA_OCC_CASES(true)
+#undef TRIA_OCC_CASES
 #undef TRIA_OCC_CASE
   if (e != hipSuccess) return -1;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -1566,28 +1767,33 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
   const long tiles = (long)a.n_units * a.hkv * a.n_tiles;
   if (tiles == 0) return hipSuccess;
   const bool paged = a.k.bt != nullptr;
-  int cap = score_capacity(d, pairing, paged, a.group);
+  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk);
   if (max_wg > 0 && max_wg < cap) cap = max_wg;
   if (cap < a.n_tiles) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
-  const size_t lds = score_lds(a.group, paged);
-#define TRIA_SCORE_CASE(DD, PP, PG)                                        \
-  if (d == DD && pairing == PP && paged == PG) {                           \
-    hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, lds, s, a);      \
-    return hipGetLastError();                                              \
+  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk);
+#define TRIA_SCORE_CASE(DD, PP, PG, MX)                                       \
+  if (d == DD && pairing == PP && paged == PG && (a.omax != 0) == MX) {      \
+    if (MX) hipLaunchKernelGGL((k_score_max<DD, PP, PG>), grid, blk, lds, s, a); \
+    else hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, lds, s, a);   \
+    return hipGetLastError();                                                 \
   }
-  TRIA_SCORE_CASE(64, 0, false)
-  TRIA_SCORE_CASE(64, 1, false)
-  TRIA_SCORE_CASE(128, 0, false)
-  TRIA_SCORE_CASE(128, 1, false)
-  TRIA_SCORE_CASE(256, 0, false)
-  TRIA_SCORE_CASE(256, 1, false)
-  TRIA_SCORE_CASE(64, 0, true)
-  TRIA_SCORE_CASE(64, 1, true)
-  TRIA_SCORE_CASE(128, 0, true)
-  TRIA_SCORE_CASE(128, 1, true)
-  TRIA_SCORE_CASE(256, 0, true)
-  TRIA_SCORE_CASE(256, 1, true)
+#define TRIA_SCORE_CASES(MX)        \
+  TRIA_SCORE_CASE(64, 0, false, MX)  \
+  TRIA_SCORE_CASE(64, 1, false, MX)  \
+  TRIA_SCORE_CASE(128, 0, false, MX) \
+  TRIA_SCORE_CASE(128, 1, false, MX) \
+  TRIA_SCORE_CASE(256, 0, false, MX) \
+  TRIA_SCORE_CASE(256, 1, false, MX) \
+  TRIA_SCORE_CASE(64, 0, true, MX)   \
+  TRIA_SCORE_CASE(64, 1, true, MX)   \
+  TRIA_SCORE_CASE(128, 0, true, MX)  \
+  TRIA_SCORE_CASE(128, 1, true, MX)  \
+  TRIA_SCORE_CASE(256, 0, true, MX)  \
+  TRIA_SCORE_CASE(256, 1, true, MX)
+  TRIA_SCORE_CASES(false)
+  TRIA_SCORE_CASES(true)
+#undef TRIA_SCORE_CASES
 #undef TRIA_SCORE_CASE
   return hipErrorInvalidValue;
 }

@@ -28,7 +28,8 @@ def params_for(cfg: synth.Config) -> L.TriaParams:
     return L.make_params(cfg.head_dim, cfg.n_kv_heads, cfg.group, cfg.n_layers,
                          L.PAIR_NEOX if cfg.pairing == "neox" else L.PAIR_INTERLEAVED,
                          L.AGG_MEAN if cfg.agg == "mean" else L.AGG_MAX,
-                         cfg.rope_base, cfg.offsets, cfg.sink, cfg.window)
+                         cfg.rope_base, cfg.offsets, cfg.sink, cfg.window,
+                         L.OFFSETS_MAX if cfg.offset_reduce == "max" else L.OFFSETS_MEAN)
 
 
 def host_cache(cfg: synth.Config, which: str, workers: int | None = None) -> np.ndarray:

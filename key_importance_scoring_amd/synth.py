@@ -65,6 +65,7 @@ class Config:
     block_size: int = 16
     nonconc_frac: float = 0.0
     seed: int = 0
+    offset_reduce: str = "mean"   # "mean" (the method) | "max": reduction over the future offsets
 
     @property
     def n_q_heads(self) -> int:

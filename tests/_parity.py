@@ -47,7 +47,7 @@ def oracle_head(cfg, unit: int, g: int, form: str = "folded", mu=None, absm=None
     pos = synth.positions(cfg, unit)
     G = cfg.group
     raw = np.stack([o.score_head(rows, pos, int(u.q_pos[unit]), mu[layer, h], absm[layer, h], cfg.head_dim,
-                                 cfg.pairing, cfg.rope_base, cfg.offsets, form)
+                                 cfg.pairing, cfg.rope_base, cfg.offsets, form, cfg.offset_reduce)
                     for h in range(g * G, (g + 1) * G)]) if n else np.zeros((G, 0))
     agg = o.aggregate_unit(raw, n, G, cfg.sink, cfg.window, cfg.agg)[0] if n else np.zeros(0)
     kept = o.select(agg, int(u.budget[unit])) if n else np.zeros(0, np.int64)

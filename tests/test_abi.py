@@ -110,6 +110,24 @@ def test_score_rejects_bad_params(kw, status):
     assert _status(lambda: _score(p=p, ws_bytes=1 << 40)) == status
 
 
+def test_score_rejects_bad_offset_reduce():
+    assert _status(lambda: _score(p=_params(offset_reduce=2), ws_bytes=1 << 40)) == L.TRIA_EINVAL
+
+
+def test_max_over_offsets_rejects_blocks_beyond_lds():
+    # d 256, G 8, 17 offsets: 8 heads x 3 blocks x 8 KiB of staged operands do not fit
+    p = _params(head_dim=256, group=8, offset_reduce=L.OFFSETS_MAX)
+    k = _view(stride_unit=8 * 4096 * 256, stride_head=4096 * 256, stride_slot=256)
+    assert _status(lambda: _score(p=p, k=k, ws_bytes=1 << 40)) == L.TRIA_ESHAPE
+
+
+def test_max_over_offsets_needs_more_workspace():
+    mean = L.tria_workspace_size(_params(), 2, 4096)
+    mx = L.tria_workspace_size(_params(offset_reduce=L.OFFSETS_MAX), 2, 4096)
+    # 2 units x 8 KV heads x 9 blocks (two offsets of the 4 heads each) x 4 chunks x 64 lanes x 16 B
+    assert mx - mean >= 2 * 8 * 9 * 4 * 64 * 16
+
+
 def test_score_rejects_empty_offsets():
     p = _params()
     p.n_offsets = 0

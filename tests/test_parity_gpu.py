@@ -95,6 +95,49 @@ def test_small_parity(name):
     _check_oracle_compaction(prob, kept)
 
 
+# maximum over the offsets: every layout of the offset blocks (a shared block of each
+# head's last offset, a padded last block per head, whole blocks only), both
+# pairings, d 64 / 128 / 256, G 3 / 4 / 8, dense and paged
+MAXO = {
+    "q8_max": C["qwen3_8b"].replace(name="q8_max", n_layers=2, n_kv=5003, budget=1000, offset_reduce="max"),
+    "lc_max": C["long_context"].replace(name="lc_max", n_kv=6000, budget=600, offset_reduce="max"),
+    "bd_max": C["batched_decode"].replace(name="bd_max", n_seqs=6, n_kv=3000, ragged_min=300,
+                                          offset_reduce="max"),
+    "d256_max": C["qwen3_8b"].replace(name="d256_max", head_dim=256, n_layers=1, n_kv_heads=2, n_kv=2500,
+                                      budget=700, offset_reduce="max"),
+    "d64_max_3off": C["tiny"].replace(name="d64_max_3off", pairing="interleaved", n_kv=3001, budget=1200,
+                                      offsets=(1, 2, 4), offset_reduce="max", agg="max"),
+    "g3_max_9off": C["long_context"].replace(name="g3_max_9off", head_dim=128, n_kv_heads=2, group=3, n_kv=2100,
+                                             budget=900, offsets=tuple(2 ** i for i in range(9)),
+                                             offset_reduce="max"),
+    "max_16off": C["qwen3_8b"].replace(name="max_16off", n_layers=1, n_kv_heads=2, n_kv=2222, budget=800,
+                                       offsets=tuple(2 ** i for i in range(16)), offset_reduce="max"),
+    "max_1off": C["tiny"].replace(name="max_1off", n_kv=1500, offsets=(64,), offset_reduce="max"),
+}
+
+
+@pytest.mark.parametrize("name", list(MAXO))
+def test_max_over_offsets_parity(name):
+    cfg = MAXO[name]
+    prob = _run(cfg)
+    assert prob.flags() == _expected_flags(cfg)
+    kept = {unit: check_unit(prob, unit, form="direct") for unit in range(cfg.n_units)}
+    _check_oracle_compaction(prob, kept)
+
+
+def test_max_over_offsets_full_size_sampled():
+    """The Qwen3-8B-shaped workload with the maximum over its 17 offsets, in the
+    benchmark's launch configuration (no per-query-head scores)."""
+    cfg = C["qwen3_8b"].replace(name="qwen3_8b_max", offset_reduce="max")
+    prob = _run(cfg, keep_raw=False)
+    assert prob.flags() == 0
+    kept = {}
+    for unit, heads in ((0, [0, 5]), (cfg.n_units - 1, [3]), (17, [7])):
+        log(f"[parity] {cfg.name}: checking unit {unit}")
+        kept[unit] = check_unit(prob, unit, heads=heads, form="direct")
+    _check_oracle_compaction(prob, kept)
+
+
 @pytest.fixture(params=[L.SELECT_TILED, L.SELECT_PER_GROUP], ids=["tiled", "per_group"])
 def strategy(request):
     prev = L.tria_select_strategy(request.param)
