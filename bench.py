@@ -364,6 +364,7 @@ def main() -> int:
     # its useful MFMA work: per (key, query head) a d-long dot product per offset
     # (maximum variant) or one folded dot product (the mean), plus the norm term's d/2
     dots = len(cfg.offsets) if cfg.offset_reduce == "max" else 1
+    score_kernel = "k_score_max" if cfg.offset_reduce == "max" else "k_score"
     score_flops = keys * cfg.group * 2 * (cfg.head_dim * dots + cfg.head_dim // 2)
     score_ms = per_kernel["k_score"]
     achieved = score_bytes / (score_ms / 1e3) / 1e9
@@ -397,9 +398,9 @@ def main() -> int:
         "kernel_timing": {"source": "HIP events on the launch stream around each library launch, over a second "
                                     "region of the same K steps after the timed one",
                           "ms_per_step_with_kernel_events": ms_inst},
-        "roofline": {"kernel": "k_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+        "roofline": {"kernel": score_kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic("k_score", cfg.name),
+                     "traffic": recorded_traffic(score_kernel, cfg.name),
                      "algorithmic_bytes_per_launch": score_bytes, "dominant_kernel": dom,
                      "mfma_bf16_tflops": score_flops / (score_ms / 1e3) / 1e12,
                      "mfma_frac_of_bf16_dense_peak": score_flops / (score_ms / 1e3) / 2.5e15},

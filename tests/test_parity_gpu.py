@@ -113,6 +113,10 @@ MAXO = {
     "max_16off": C["qwen3_8b"].replace(name="max_16off", n_layers=1, n_kv_heads=2, n_kv=2222, budget=800,
                                        offsets=tuple(2 ** i for i in range(16)), offset_reduce="max"),
     "max_1off": C["tiny"].replace(name="max_1off", n_kv=1500, offsets=(64,), offset_reduce="max"),
+    "g1_max": C["qwen3_8b"].replace(name="g1_max", n_layers=1, n_kv_heads=3, group=1, n_kv=2300, budget=400,
+                                    offset_reduce="max"),
+    "g7_max": C["qwen3_8b"].replace(name="g7_max", n_layers=1, n_kv_heads=2, group=7, n_kv=2222, budget=800,
+                                    agg="mean", offset_reduce="max"),
 }
 
 
