@@ -265,6 +265,101 @@ def bench_calibrate(args) -> int:
     return 0
 
 
+DECODE_METRIC = "M keys scored+selected+compacted/s in a decode loop (prune every 128 tokens); % of HBM peak GB/s"
+
+
+def bench_decode(args) -> int:
+    """The decode loop: 64 sequences x 8 KV heads (d 128, G 4, NEOX) hold a budget of
+    2048 slots; every step appends 128 tokens to each and prunes them back in place
+    (score -> select -> in-place compaction), the port's regime (interval 128, window
+    256, sink 0).  A step's new rows are resident in HBM before the timed region."""
+    import numpy as np
+    import torch
+    from key_importance_scoring_amd import _lib as L
+    from key_importance_scoring_amd import synth
+    from key_importance_scoring_amd.decode import DecodeLoop
+
+    cfg = synth.CONFIGS["batched_decode"].replace(name="decode_loop", n_seqs=64, ragged_min=0, window=256, sink=0,
+                                                  offset_reduce=args.offsets)
+    budget, interval = 2048, 128
+    loop = DecodeLoop(cfg, budget, interval)
+    n_fill = -(-budget // interval)                      # appends until the first prune
+    n_steps = n_fill + args.warmup + 2 * args.steps     # the fill, warm-up and both timed regions
+    print(f"[bench] decode loop: generating {n_steps} steps of rows", file=sys.stderr, flush=True)
+    rows = [loop.upload(*loop.new_rows(interval, p0=i * interval)) for i in range(n_steps)]
+    for i in range(n_fill):
+        loop.step(rows=rows[i])
+    for i in range(n_fill, n_fill + args.warmup):
+        loop.step(rows=rows[i])
+    torch.cuda.synchronize()
+    assert loop.prunes >= 1
+
+    stream = torch.cuda.current_stream()
+
+    def region(kernel_events: bool, first: int):
+        L.tria_timing_read()
+        L.tria_timing_enable(kernel_events)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(first, first + args.steps):
+            assert loop.step(rows=rows[i], stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        L.tria_timing_enable(False)
+        return t0.elapsed_time(t1) / args.steps, L.tria_timing_read()
+
+    ms, _ = region(False, n_fill + args.warmup)
+    ms_inst, kt = region(True, n_fill + args.warmup + args.steps)
+    assert loop.flags() == 0
+    per_kernel = {k: v[0] / v[1] for k, v in kt.items() if v[1]}
+    U, Hkv, d = cfg.n_units, cfg.n_kv_heads, cfg.head_dim
+    n = budget + interval
+    keys = U * Hkv * n                                   # head-keys scored per prune
+    score_bytes = keys * 2 * d
+    # compaction: every kept row that moves is read and written (K and V) with its
+    # position; at most all of them
+    cmp_bytes = U * Hkv * budget * (4 * 2 * d + 8)
+    alg = score_bytes + cmp_bytes + U * Hkv * interval * (4 * d + 4)   # + the appended rows
+    # the dominant kernel is the in-place compaction (its timing id is k_compact):
+    # nearly every kept row moves when the evicted slots are spread out
+    cmp_ms = per_kernel["k_compact"]
+    achieved = cmp_bytes / (cmp_ms / 1e3) / 1e9
+    print(f"[bench] {ms:.4f} ms/step ({ms_inst:.4f} with events), kernels {per_kernel}", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": DECODE_METRIC,
+        "value": keys / (ms / 1e3) / 1e6,
+        "unit": "M keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_loop", "sequences": U, "kv_heads": Hkv, "q_heads": cfg.n_q_heads,
+                   "head_dim": d, "budget": budget, "interval": interval, "window": cfg.window, "sink": cfg.sink,
+                   "paged": True, "block_size": cfg.block_size, "offset_reduce": cfg.offset_reduce,
+                   "step": "append 128 tokens per sequence + prune in place"},
+        "prune_overhead_us_per_generated_token": ms * 1e3 / interval,
+        "hbm_algorithmic_GBps_upper_bound": alg / (ms / 1e3) / 1e9,
+        "algorithmic_bytes_per_step_upper_bound": alg,
+        "kernel_ms": per_kernel,
+        "roofline": {"kernel": "k_compact_inplace", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic("k_compact_inplace", "decode_loop"),
+                     "algorithmic_bytes_per_launch": cmp_bytes,
+                     "algorithmic_bytes_note": "every kept row's K and V read and written with its position (an "
+                                               "upper bound: rows whose slot does not change are not moved)",
+                     "score_kernel_GBps": score_bytes / (per_kernel["k_score"] / 1e3) / 1e9},
+        "cpu_baseline": None,
+    }))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +376,8 @@ def main() -> int:
                     help="instead of the pass, time the calibration reduction (tria_calibrate) over a "
                          "synthetic pre-RoPE query stream of --tokens rows per (layer, query head)")
     ap.add_argument("--tokens", type=int, default=8192, help="calibration tokens (with --calibrate)")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="instead of the single pass, time the decode loop (append 128 tokens, prune in place)")
     ap.add_argument("--offsets", choices=("mean", "max"), default="mean",
                     help="reduction over the future offsets: the mean (the method) or the maximum variant")
     args = ap.parse_args()
@@ -299,6 +396,8 @@ def main() -> int:
         return copy_probe(args.copy_probe, args.steps)
     if args.calibrate:
         return bench_calibrate(args)
+    if args.decode_loop:
+        return bench_decode(args)
     from key_importance_scoring_amd import _lib as L
     from key_importance_scoring_amd import synth
     from key_importance_scoring_amd.device import DeviceProblem

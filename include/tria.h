@@ -229,6 +229,42 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
                          const tria_kv_view* k_dst, const tria_kv_view* v_dst, int32_t* pos_dst,
                          void* stream);
 
+/* tria_compact_inplace - tria_compact into the cache it reads from, for a decode
+ * loop that prunes a sequence every so many generated tokens and keeps its blocks
+ * [Calib issue: the port scores every 128 tokens, interval=128; README mirror:
+ * the KV budget].  For unit u, KV head g and j < cnt[u]:
+ *   K row (u, g, j) <- K row (u, g, idx[u][g][j]);  V likewise;
+ *   pos[u][g][j] <- pos[u][g][idx[u][g][j]]   (when pos is not NULL)
+ * with idx as tria_select writes it: ascending, so idx[j] >= j.  Rows with
+ * idx[j] == j are not touched; slots >= cnt[u] keep whatever they held.
+ *   k, v        [device] cache views (dense or paged; the same layouts as
+ *               tria_compact's sources), read and written
+ *   pos         [device] int32 [U][Hkv][n_max] per-head positions, or NULL
+ *   len, idx, cnt, b_max, n_max as for tria_compact
+ * Each (unit, KV head) is moved by one workgroup in ascending chunks of 128 rows,
+ * a chunk's reads completing before its writes: with ascending indices no row is
+ * overwritten before it is read.  An index that is not ascending, below its row
+ * or outside [0, len[u]) is flagged (TRIA_FLAG_INDEX) and its row left in place
+ * (the head's result is then unspecified).  Errors as tria_compact.  K and V
+ * views must not overlap each other.
+ */
+tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
+                                 int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+                                 const int32_t* idx, const int32_t* cnt, void* ws, void* stream);
+
+/* tria_append - writes t_new new rows per (unit, KV head) at slots len[u] ..
+ * len[u] + t_new - 1 (the decode loop's generated tokens; the caller advances len
+ * afterwards).
+ *   k_new, v_new [device] bf16 [U][Hkv][t_new][d], rows already rotated at their
+ *               positions (as a model caches them)
+ *   pos_new     [device] int32 [U][t_new] their positions, written to every
+ *               head's row of pos ([U][Hkv][n_max]); both may be NULL
+ * Slots at or past n_max are flagged (TRIA_FLAG_LEN) and skipped.
+ */
+tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
+                        int32_t n_units, int32_t n_max, const int32_t* len, int32_t t_new, const void* k_new,
+                        const void* v_new, const int32_t* pos_new, void* ws, void* stream);
+
 /* tria_calibrate - the calibrated query statistics tria_score reads, from a stream
  * of pre-RoPE query rows [Calib issue, "How it works": per (layer, head, band)
  * means in the RoPE complex pairing; Blog, the calibration step].

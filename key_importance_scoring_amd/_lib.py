@@ -24,7 +24,7 @@ FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
            "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name",
            "tria_score_max_workgroups", "tria_select_strategy", "tria_calibrate_workspace_size",
-           "tria_calibrate")
+           "tria_calibrate", "tria_compact_inplace", "tria_append")
 
 
 class TriaError(RuntimeError):
@@ -97,6 +97,13 @@ def load() -> ctypes.CDLL:
     lib.tria_calibrate.restype = c_int32
     lib.tria_calibrate.argtypes = [POINTER(TriaParams), c_void_p, c_int64, c_int64, c_int64, c_int32,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.tria_compact_inplace.restype = c_int32
+    lib.tria_compact_inplace.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_void_p,
+                                         c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p]
+    lib.tria_append.restype = c_int32
+    lib.tria_append.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_void_p, c_int32,
+                                c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     _lib = lib
     return lib
 
@@ -179,6 +186,18 @@ def tria_calibrate(p: TriaParams, q, stride_layer: int, stride_head: int, stride
     _check(load().tria_calibrate(ctypes.byref(p), ptr(q), stride_layer, stride_head, stride_token, n_tokens,
                                  ptr(q_mean_re), ptr(q_mean_im), ptr(q_abs_mean), ptr(r), ptr(mrl), ptr(ws),
                                  ws_bytes, stream_handle(stream)))
+
+
+def tria_compact_inplace(p: TriaParams, k: TriaKvView, v: TriaKvView, pos, n_units: int, n_max: int, b_max: int,
+                         len_, idx, cnt, ws, stream=None) -> None:
+    _check(load().tria_compact_inplace(ctypes.byref(p), ctypes.byref(k), ctypes.byref(v), ptr(pos), n_units, n_max,
+                                       b_max, ptr(len_), ptr(idx), ptr(cnt), ptr(ws), stream_handle(stream)))
+
+
+def tria_append(p: TriaParams, k: TriaKvView, v: TriaKvView, pos, n_units: int, n_max: int, len_, t_new: int,
+                k_new, v_new, pos_new, ws, stream=None) -> None:
+    _check(load().tria_append(ctypes.byref(p), ctypes.byref(k), ctypes.byref(v), ptr(pos), n_units, n_max, ptr(len_),
+                              t_new, ptr(k_new), ptr(v_new), ptr(pos_new), ptr(ws), stream_handle(stream)))
 
 
 def tria_device_flags(ws, stream=None) -> int:

@@ -374,6 +374,50 @@ tria_status tria_calibrate(const tria_params* p, const void* q, int64_t stride_l
   return launch_status(e, "k_calib");
 }
 
+tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
+                                 int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+                                 const int32_t* idx, const int32_t* cnt, void* ws, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
+  if ((st = check_view(k, "k", p->head_dim, n_max)) != TRIA_OK) return st;
+  if ((st = check_view(v, "v", p->head_dim, n_max)) != TRIA_OK) return st;
+  if (!len || !idx || !cnt) return fail(TRIA_EINVAL, "a required device pointer is NULL");
+  if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL (its flag word records contract violations)");
+  if (n_units == 0 || b_max == 0 || n_max == 0) return TRIA_OK;
+  if (!k->block_table && !v->block_table) {
+    uintptr_t a0, a1, b0, b1;
+    dense_range(k, n_units, p->n_kv_heads, n_max, p->head_dim, a0, a1);
+    dense_range(v, n_units, p->n_kv_heads, n_max, p->head_dim, b0, b1);
+    if (overlaps(a0, a1, b0, b1)) return fail(TRIA_EOVERLAP, "k and v overlap");
+  }
+  tria::InplaceArgs ia{mkview(k), mkview(v), pos, n_units, n_max, b_max, p->n_kv_heads, p->head_dim,
+                       len, idx, cnt, static_cast<int32_t*>(ws)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(kIdCompact, s, [&] { return tria::launch_compact_inplace(ia, s); });
+  return launch_status(e, "k_compact_inplace");
+}
+
+tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
+                        int32_t n_units, int32_t n_max, const int32_t* len, int32_t t_new, const void* k_new,
+                        const void* v_new, const int32_t* pos_new, void* ws, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_units < 0 || n_max < 0 || t_new < 0) return fail(TRIA_EINVAL, "n_units, n_max and t_new must be >= 0");
+  if ((st = check_view(k, "k", p->head_dim, n_max)) != TRIA_OK) return st;
+  if ((st = check_view(v, "v", p->head_dim, n_max)) != TRIA_OK) return st;
+  if (!len || !k_new || !v_new) return fail(TRIA_EINVAL, "a required device pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+    return fail(TRIA_ESHAPE, "k_new and v_new must be 16-byte aligned");
+  if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL (its flag word records contract violations)");
+  if (n_units == 0 || t_new == 0) return TRIA_OK;
+  tria::AppendArgs aa{mkview(k), mkview(v), pos, n_units, n_max, p->n_kv_heads, p->head_dim, t_new, len,
+                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), pos_new,
+                      static_cast<int32_t*>(ws)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(tria::launch_append(aa, s), "k_append");
+}
+
 tria_status tria_device_flags(void* ws, int32_t* flags, void* stream) {
   if (!ws || !flags) return fail(TRIA_EINVAL, "ws and flags must be non-NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);

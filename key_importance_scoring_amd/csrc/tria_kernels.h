@@ -188,4 +188,31 @@ hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 
+// In-place compaction (the decode loop): row j <- row idx[j], j < cnt[u], in the
+// cache it reads from.
+constexpr int kInplaceRows = 128;       // rows per chunk (one workgroup per (unit, KV head) walks them in order)
+struct InplaceArgs {
+  MutKView k, v;
+  int32_t* pos;               // [U][Hkv][n_max] per-head positions, or null
+  int32_t n_units, n_max, b_max, hkv, d;
+  const int32_t* len;
+  const int32_t* idx;         // [U][Hkv][b_max]
+  const int32_t* cnt;
+  int32_t* flags;
+};
+hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s);
+
+// Appends t_new rows per (unit, KV head) at slots len[u] .. len[u] + t_new - 1.
+struct AppendArgs {
+  MutKView k, v;
+  int32_t* pos;               // [U][Hkv][n_max] or null
+  int32_t n_units, n_max, hkv, d, t_new;
+  const int32_t* len;
+  const uint16_t* k_new;      // [U][Hkv][t_new][d]
+  const uint16_t* v_new;      // [U][Hkv][t_new][d]
+  const int32_t* pos_new;     // [U][t_new] or null
+  int32_t* flags;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
 }  // namespace tria

@@ -1697,6 +1697,108 @@ __global__ __launch_bounds__(256) void k_calib_final(CalibArgs a) {
   if (a.mrl) a.mrl[o] = (float)(sqrt(sf[3] * sf[3] + sf[4] * sf[4]) / T);
 }
 
+// ============================================================================ decode loop
+// In place: for every (unit, KV head), row j <- row idx[j] for j < cnt[u] (K, V and,
+// when given, the head's position), in the cache the rows are read from, so that a
+// pruned sequence keeps its own blocks.  The kept slots ascend and idx[j] >= j, so
+// the rows written by chunk c (j in [c C, c C + C)) are read only by chunks <= c:
+// one workgroup per (unit, KV head) walks the chunks in order, and each chunk's
+// reads all complete (every load waited for, then a barrier) before any of its
+// writes.  A chunk issues its indices', its source block ids' and its rows' loads
+// each together.  Rows with idx[j] == j stay where they are.  An index that breaks
+// the order (not ascending, below j, or outside [0, len[u])) is flagged and its row
+// left as it is.
+template <int D>
+__global__ __launch_bounds__(256) void k_compact_inplace(InplaceArgs a) {
+  constexpr int LPR = D / 8, RPP = 256 / LPR, NP = kInplaceRows / RPP;
+  const int ug = blockIdx.x, u = ug / a.hkv, g = ug % a.hkv;
+  const int n = min(max(a.len[u], 0), a.n_max);
+  const int K = min(max(a.cnt[u], 0), min(a.b_max, n));
+  const int part = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  const int32_t* ix = a.idx + (size_t)ug * a.b_max;
+  int32_t* ps = a.pos ? a.pos + (size_t)ug * a.n_max : nullptr;
+  for (int c0 = 0; c0 < K; c0 += kInplaceRows) {
+    int sl[NP], pr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int j = min(c0 + r0 + p * RPP, K - 1);
+      sl[p] = ix[j];
+      pr[p] = j > 0 ? ix[j - 1] : -1;
+    }
+    bool mv[NP];
+    int kb[NP], vb[NP];   // paged: the source rows' block ids (slot 0's for rows that stay)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int j = c0 + r0 + p * RPP;
+      const bool ok = sl[p] >= j && sl[p] < n && (j == 0 || sl[p] > pr[p]);
+      if (j < K && !ok && part == 0) raise_flag(a.flags, kFlagIndex);
+      mv[p] = j < K && ok && sl[p] != j;
+      const int ss = mv[p] ? sl[p] : 0;
+      kb[p] = a.k.bt ? a.k.bt[(int64_t)u * a.k.mb + ss / a.k.bs] : 0;
+      vb[p] = a.v.bt ? a.v.bt[(int64_t)u * a.v.mb + ss / a.v.bs] : 0;
+    }
+    const uint16_t* kp[NP];
+    const uint16_t* vp[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const bool kbad = a.k.bt && (kb[p] < 0 || kb[p] >= a.k.npb);
+      const bool vbad = a.v.bt && (vb[p] < 0 || vb[p] >= a.v.npb);
+      if (mv[p] && (kbad || vbad) && part == 0) raise_flag(a.flags, kFlagBlock);
+      mv[p] = mv[p] && !kbad && !vbad;
+      const int ss = sl[p];
+      kp[p] = a.k.bt ? a.k.base + ((int64_t)kb[p] * a.k.bs + ss % a.k.bs) * a.k.ss + (int64_t)g * a.k.sh
+                     : a.k.base + (int64_t)u * a.k.su + (int64_t)g * a.k.sh + (int64_t)ss * a.k.ss;
+      vp[p] = a.v.bt ? a.v.base + ((int64_t)vb[p] * a.v.bs + ss % a.v.bs) * a.v.ss + (int64_t)g * a.v.sh
+                     : a.v.base + (int64_t)u * a.v.su + (int64_t)g * a.v.sh + (int64_t)ss * a.v.ss;
+    }
+    u32x4 kr[NP], vr[NP];
+    int pv[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (mv[p]) {
+        kr[p] = reinterpret_cast<const u32x4*>(kp[p])[part];
+        vr[p] = reinterpret_cast<const u32x4*>(vp[p])[part];
+        pv[p] = ps ? ps[sl[p]] : 0;
+      }
+    }
+    // every read of this chunk has returned before any thread writes it
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (!mv[p]) continue;
+      const int j = c0 + r0 + p * RPP;
+      uint16_t* kd = const_cast<uint16_t*>(row_ptr(a.k, u, g, j, a.flags));
+      uint16_t* vd = const_cast<uint16_t*>(row_ptr(a.v, u, g, j, a.flags));
+      if (kd) reinterpret_cast<u32x4*>(kd)[part] = kr[p];
+      if (vd) reinterpret_cast<u32x4*>(vd)[part] = vr[p];
+      if (ps && part == 0) ps[j] = pv[p];
+    }
+  }
+}
+
+// Appends t_new rows of each (unit, KV head) at slots len[u] + t (K, V and the
+// unit's positions into every head's position row); slots past n_max are flagged.
+__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+  const int ug = blockIdx.x, u = ug / a.hkv, g = ug % a.hkv;
+  const int lpr = a.d / 8, rpp = 256 / lpr;
+  const int part = threadIdx.x % lpr;
+  const int n0 = max(a.len[u], 0);
+  for (int t = blockIdx.y * rpp + threadIdx.x / lpr; t < a.t_new; t += gridDim.y * rpp) {
+    const int sl = n0 + t;
+    if (sl >= a.n_max) {
+      if (part == 0) raise_flag(a.flags, kFlagLen);
+      continue;
+    }
+    const size_t src = ((size_t)ug * a.t_new + t) * a.d;
+    uint16_t* kd = const_cast<uint16_t*>(row_ptr(a.k, u, g, sl, a.flags));
+    uint16_t* vd = const_cast<uint16_t*>(row_ptr(a.v, u, g, sl, a.flags));
+    if (kd) reinterpret_cast<u32x4*>(kd)[part] = reinterpret_cast<const u32x4*>(a.k_new + src)[part];
+    if (vd) reinterpret_cast<u32x4*>(vd)[part] = reinterpret_cast<const u32x4*>(a.v_new + src)[part];
+    if (a.pos && a.pos_new && part == 0) a.pos[(size_t)ug * a.n_max + sl] = a.pos_new[(size_t)u * a.t_new + t];
+  }
+}
+
 // ============================================================================ launches
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   if (a.n_units == 0) return hipSuccess;
@@ -1874,6 +1976,24 @@ hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s) {
   TRIA_CALIB_CASE(256, 1)
 #undef TRIA_CALIB_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s) {
+  if (a.n_units == 0 || a.hkv == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.n_units * a.hkv));
+  if (a.d == 64) hipLaunchKernelGGL(k_compact_inplace<64>, grid, dim3(256), 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL(k_compact_inplace<128>, grid, dim3(256), 0, s, a);
+  else if (a.d == 256) hipLaunchKernelGGL(k_compact_inplace<256>, grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.n_units == 0 || a.hkv == 0 || a.t_new == 0) return hipSuccess;
+  const int rpp = 256 / (a.d / 8);
+  const unsigned gy = (unsigned)min((a.t_new + rpp - 1) / rpp, 64);
+  hipLaunchKernelGGL(k_append, dim3((unsigned)(a.n_units * a.hkv), gy), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace tria

@@ -38,7 +38,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # stream kinds for SeedSequence
-_K_CENTRE, _K_NOISE, _V_ROWS, _Q_STATS, _LENGTHS, _BLOCKS, _NONCONC, _Q_ROWS = range(8)
+_K_CENTRE, _K_NOISE, _V_ROWS, _Q_STATS, _LENGTHS, _BLOCKS, _NONCONC, _Q_ROWS, _DEC_K, _DEC_V = range(10)
 
 
 @dataclass(frozen=True)
@@ -260,6 +260,28 @@ def key_rows(cfg: Config, unit: int, kv_head: int) -> np.ndarray:
     ra = a * cos - b * sin
     rb = a * sin + b * cos
     return f32_to_bf16_bits(_layout(ra, rb, cfg.pairing).astype(np.float32))
+
+
+def decode_rows(cfg: Config, unit: int, kv_head: int, p0: int, count: int, which: str) -> np.ndarray:
+    """uint16 [count][d]: bf16 bits of the keys (``"k"``) or values (``"v"``) that a
+    decode loop appends for the tokens at positions p0 .. p0 + count - 1 of one
+    (unit, KV head).  Keys are drawn like the cache's (the (layer, KV head) centre
+    plus N(0, 0.3^2) per component, rotated at their positions), values N(0, 1);
+    each chunk is seeded by (unit, KV head, p0), so a chunk can be redrawn alone."""
+    F = cfg.head_dim // 2
+    if which == "v":
+        rng = _rng(cfg, _DEC_V, unit * 4096 + kv_head, p0)
+        return f32_to_bf16_bits(rng.standard_normal((count, cfg.head_dim), dtype=np.float32))
+    layer = int(units(cfg).unit_layer[unit])
+    c = key_centres(cfg, layer, kv_head)
+    rng = _rng(cfg, _DEC_K, unit * 4096 + kv_head, p0)
+    noise = rng.standard_normal((2, count, F)) * 0.3
+    a = c.real[None, :] + noise[0]
+    b = c.imag[None, :] + noise[1]
+    inv_freq = cfg.rope_base ** (-(2.0 * np.arange(F, dtype=np.float64)) / cfg.head_dim)
+    ang = np.outer(np.arange(p0, p0 + count, dtype=np.float64), inv_freq)
+    cos, sin = np.cos(ang), np.sin(ang)
+    return f32_to_bf16_bits(_layout(a * cos - b * sin, a * sin + b * cos, cfg.pairing).astype(np.float32))
 
 
 def query_rows(cfg: Config, layer: int, q_head: int, n_tokens: int) -> np.ndarray:

@@ -266,3 +266,30 @@ def test_calibrate_checks():
     # more (layer, query head) pairs than one launch dimension holds
     big = _params(n_layers=2100, n_kv_heads=8, group=4)
     assert _status(lambda: _calibrate(p=big, ws_bytes=1 << 40)) == L.TRIA_ESHAPE
+
+
+def test_compact_inplace_checks():
+    p = _params()
+    k = _view(A)
+    v = _view(A + 2 * 8 * 4096 * 128 * 2)
+    call = lambda **kw: L.tria_compact_inplace(kw.get("p", p), kw.get("k", k), kw.get("v", v), None, kw.get("U", 2),
+                                               4096, 2048, kw.get("len_", A), A, A, kw.get("ws", WS))
+    assert _status(lambda: call(len_=None)) == L.TRIA_EINVAL
+    assert _status(lambda: call(ws=None)) == L.TRIA_EWORKSPACE
+    assert _status(lambda: call(p=_params(pairing=9))) == L.TRIA_EINVAL
+    assert _status(lambda: call(k=_view(A + 8))) == L.TRIA_ESHAPE
+    assert _status(lambda: call(v=_view(A + 4096))) == L.TRIA_EOVERLAP      # K and V overlap
+    call(U=0)                                                                  # nothing to do
+
+
+def test_append_checks():
+    p = _params()
+    k = _view(A)
+    v = _view(A + 2 * 8 * 4096 * 128 * 2)
+    call = lambda **kw: L.tria_append(p, k, v, None, 2, 4096, A, kw.get("t", 128), kw.get("kn", A), A, None,
+                                      kw.get("ws", WS))
+    assert _status(lambda: call(kn=None)) == L.TRIA_EINVAL
+    assert _status(lambda: call(kn=A + 8)) == L.TRIA_ESHAPE
+    assert _status(lambda: call(t=-1)) == L.TRIA_EINVAL
+    assert _status(lambda: call(ws=None)) == L.TRIA_EWORKSPACE
+    call(t=0)
