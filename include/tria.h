@@ -302,6 +302,54 @@ tria_status tria_calibrate(const tria_params* p, const void* q, int64_t stride_l
                            int64_t stride_token, int32_t n_tokens, float* q_mean_re, float* q_mean_im,
                            float* q_abs_mean, float* r, float* mrl, void* ws, size_t ws_bytes, void* stream);
 
+/* TRIA statistics files [Calib issue: the port's loader takes a stats file with
+ * magic 0x54524941 and versions 1..3, whose header gives the layer count, the KV
+ * head count, fc (bands per head), head_dim, optional layer budget scales, and
+ * per-head records of E[Re q_f], E[Im q_f], E|q_f| and an MRL field the loader
+ * skips; layer budget scales default to 1.0].  The pages give neither the byte
+ * order nor the field order; this library reads and writes little-endian:
+ *   u32 magic, u32 version, u32 n_layers, u32 n_heads (query heads),
+ *   u32 n_kv_heads, u32 fc;  version >= 2: u32 head_dim (= 2 fc);
+ *   version >= 3: u32 flags (bit 0: f32 layer_budget_scales[n_layers] follow);
+ *   then per (layer, query head), layer-major: f32 q_mean_real[fc],
+ *   f32 q_mean_imag[fc], f32 q_abs_mean[fc], and (version >= 2) f32 mrl[fc].
+ * Host memory only; no GPU work. */
+typedef struct tria_stats_info {
+  uint32_t version, n_layers, n_heads, n_kv_heads, fc, head_dim;
+  int32_t has_budget_scales;   /* version 3 with the scales present             */
+  int32_t mrl_present;         /* version >= 2                                   */
+} tria_stats_info;
+
+/* Parses n_bytes of a stats file.  The statistics arrays, when not NULL, receive
+ * [n_layers][n_heads][fc] floats each (the layout tria_score reads); mrl zeros for
+ * version 1; layer_budget_scales [n_layers] (1.0 where the file has none).  Returns
+ * TRIA_EINVAL for a wrong magic, version or flag, TRIA_ESHAPE for inconsistent or
+ * truncated data (the size must match the header exactly). */
+tria_status tria_stats_parse(const void* bytes, size_t n_bytes, tria_stats_info* info, float* q_mean_re,
+                             float* q_mean_im, float* q_abs_mean, float* mrl, float* layer_budget_scales);
+
+/* Writes a stats file of info->version into out (cap bytes) and returns its size;
+ * with out NULL or cap too small it writes nothing and returns the size needed; 0
+ * for invalid arguments.  mrl may be NULL (zeros); layer_budget_scales is written
+ * for version 3 when info->has_budget_scales is set. */
+size_t tria_stats_encode(const tria_stats_info* info, const float* q_mean_re, const float* q_mean_im,
+                         const float* q_abs_mean, const float* mrl, const float* layer_budget_scales, void* out,
+                         size_t cap);
+
+/* Folds a per-band mask m_f >= 0 into statistics of n_rows (layer, head) rows, in
+ * place: E[q_f] <- m_f E[q_f] and E|q_f| <- E|q_f| + (m_f - 1) |E[q_f]|, so that
+ * the trigonometric term of band f is scaled by m_f while the norm weight
+ * E|q_f| - |E q_f| is unchanged [Fold note, sec. 7: the offset-independent
+ * high-frequency mask multiplies ||mu'_f|| and commutes with the fold].  Host
+ * arrays [n_rows][fc]. */
+tria_status tria_stats_band_mask(int32_t n_rows, int32_t fc, const float* mask, float* q_mean_re, float* q_mean_im,
+                                 float* q_abs_mean);
+
+/* budgets[u] = round(budget * layer_budget_scales[unit_layer[u]]) for tria_select's
+ * per-unit budgets [Calib issue: layer budget scales, 1.0 = uniform].  Host arrays. */
+tria_status tria_stats_layer_budgets(int32_t n_units, const int32_t* unit_layer, int32_t n_layers,
+                                     const float* layer_budget_scales, int32_t budget, int32_t* budgets);
+
 /* Caps the number of workgroups tria_score's persistent kernel launches (0, the
  * default, means as many as the device holds at once), for callers that keep
  * compute units free for work on other streams.  A cap below the score tiles of

@@ -13,6 +13,8 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
 
+import numpy as np
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtria.so")
 
 TRIA_OK, TRIA_EINVAL, TRIA_ESHAPE, TRIA_EBUDGET, TRIA_EOVERLAP, TRIA_EWORKSPACE, TRIA_ELAUNCH = range(7)
@@ -24,7 +26,8 @@ FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
            "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name",
            "tria_score_max_workgroups", "tria_select_strategy", "tria_calibrate_workspace_size",
-           "tria_calibrate", "tria_compact_inplace", "tria_append")
+           "tria_calibrate", "tria_compact_inplace", "tria_append", "tria_stats_parse", "tria_stats_encode",
+           "tria_stats_band_mask", "tria_stats_layer_budgets")
 
 
 class TriaError(RuntimeError):
@@ -44,6 +47,12 @@ class TriaKvView(ctypes.Structure):
     _fields_ = [("base", c_void_p), ("stride_unit", c_int64), ("stride_head", c_int64), ("stride_slot", c_int64),
                 ("block_table", c_void_p), ("block_size", c_int32), ("max_blocks", c_int32),
                 ("n_pool_blocks", c_int64)]
+
+
+class TriaStatsInfo(ctypes.Structure):
+    _fields_ = [("version", ctypes.c_uint32), ("n_layers", ctypes.c_uint32), ("n_heads", ctypes.c_uint32),
+                ("n_kv_heads", ctypes.c_uint32), ("fc", ctypes.c_uint32), ("head_dim", ctypes.c_uint32),
+                ("has_budget_scales", c_int32), ("mrl_present", c_int32)]
 
 
 _lib = None
@@ -104,6 +113,16 @@ def load() -> ctypes.CDLL:
     lib.tria_append.restype = c_int32
     lib.tria_append.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_void_p, c_int32,
                                 c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.tria_stats_parse.restype = c_int32
+    lib.tria_stats_parse.argtypes = [c_void_p, c_size_t, POINTER(TriaStatsInfo), c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p]
+    lib.tria_stats_encode.restype = c_size_t
+    lib.tria_stats_encode.argtypes = [POINTER(TriaStatsInfo), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_size_t]
+    lib.tria_stats_band_mask.restype = c_int32
+    lib.tria_stats_band_mask.argtypes = [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.tria_stats_layer_budgets.restype = c_int32
+    lib.tria_stats_layer_budgets.argtypes = [c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p]
     _lib = lib
     return lib
 
@@ -231,3 +250,79 @@ def tria_timing_read() -> dict:
     cnt = (c_int64 * n)()
     k = int(lib.tria_timing_read(ms, cnt, n))
     return {lib.tria_kernel_name(i).decode(): (ms[i], int(cnt[i])) for i in range(k)}
+
+
+# ----------------------------------------------------------------------------- statistics files (host memory)
+
+def _host_f32(a, shape=None):
+    """A C-contiguous float32 numpy array (the caller's own when it already is one)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if shape is not None and a.shape != tuple(shape):
+        a = a.reshape(shape)
+    return a
+
+
+def _np_ptr(a) -> int | None:
+    return None if a is None else a.ctypes.data
+
+
+def tria_stats_parse(data: bytes):
+    """(info, q_mean_re, q_mean_im, q_abs_mean, mrl, layer_budget_scales): the
+    statistics as float32 [n_layers][n_heads][fc], the scales as [n_layers]."""
+    lib = load()
+    buf = ctypes.create_string_buffer(bytes(data), len(data) + 1)     # never NULL, also for b""
+    info = TriaStatsInfo()
+    # first call: the header only (NULL outputs)
+    _check(lib.tria_stats_parse(buf, len(data), ctypes.byref(info), None, None, None, None, None))
+    shape = (info.n_layers, info.n_heads, info.fc)
+    re, im, ab, mrl = (np.empty(shape, np.float32) for _ in range(4))
+    scales = np.empty(info.n_layers, np.float32)
+    _check(lib.tria_stats_parse(buf, len(data), ctypes.byref(info), _np_ptr(re), _np_ptr(im), _np_ptr(ab),
+                                _np_ptr(mrl), _np_ptr(scales)))
+    return info, re, im, ab, mrl, scales
+
+
+def tria_stats_encode(version: int, n_kv_heads: int, q_mean_re, q_mean_im, q_abs_mean, mrl=None,
+                      layer_budget_scales=None) -> bytes:
+    """A stats file of the given version from float32 [n_layers][n_heads][fc] arrays."""
+    re = _host_f32(q_mean_re)
+    n_layers, n_heads, fc = re.shape
+    im = _host_f32(q_mean_im, re.shape)
+    ab = _host_f32(q_abs_mean, re.shape)
+    mr = None if mrl is None else _host_f32(mrl, re.shape)
+    sc = None if layer_budget_scales is None else _host_f32(layer_budget_scales, (n_layers,))
+    info = TriaStatsInfo(version, n_layers, n_heads, n_kv_heads, fc, 2 * fc, int(sc is not None), int(version >= 2))
+    lib = load()
+    need = int(lib.tria_stats_encode(ctypes.byref(info), _np_ptr(re), _np_ptr(im), _np_ptr(ab), _np_ptr(mr),
+                                     _np_ptr(sc), None, 0))
+    if need == 0:
+        raise TriaError(TRIA_EINVAL, "invalid stats header or arrays")
+    out = np.empty(need, np.uint8)
+    got = int(lib.tria_stats_encode(ctypes.byref(info), _np_ptr(re), _np_ptr(im), _np_ptr(ab), _np_ptr(mr),
+                                    _np_ptr(sc), _np_ptr(out), need))
+    assert got == need
+    return out.tobytes()
+
+
+def tria_stats_band_mask(mask, q_mean_re, q_mean_im, q_abs_mean) -> None:
+    """In place on C-contiguous float32 arrays [..][fc]; mask is [fc]."""
+    for a in (q_mean_re, q_mean_im, q_abs_mean):
+        if not (isinstance(a, np.ndarray) and a.dtype == np.float32 and a.flags.c_contiguous and a.flags.writeable):
+            raise TypeError("statistics must be writable C-contiguous float32 numpy arrays")
+        if a.shape != q_mean_re.shape:
+            raise ValueError("statistics arrays differ in shape")
+    fc = q_mean_re.shape[-1]
+    m = _host_f32(mask)
+    if m.shape != (fc,):
+        raise ValueError(f"mask has shape {m.shape}, expected ({fc},)")
+    _check(load().tria_stats_band_mask(q_mean_re.size // fc, fc, _np_ptr(m), _np_ptr(q_mean_re),
+                                       _np_ptr(q_mean_im), _np_ptr(q_abs_mean)))
+
+
+def tria_stats_layer_budgets(unit_layer, layer_budget_scales, budget: int):
+    """int32 [n_units] per-unit budgets for tria_select."""
+    ul = np.ascontiguousarray(unit_layer, dtype=np.int32)
+    sc = _host_f32(layer_budget_scales)
+    out = np.empty(ul.size, np.int32)
+    _check(load().tria_stats_layer_budgets(ul.size, _np_ptr(ul), sc.size, _np_ptr(sc), int(budget), _np_ptr(out)))
+    return out

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "tria_kernels.h"
+#include "tria_host.h"
 
 namespace {
 
@@ -26,6 +27,12 @@ tria_status fail(tria_status s, const char* fmt, ...) {
   va_end(ap);
   return s;
 }
+
+}  // namespace
+
+void tria::set_last_error(const char* msg) { snprintf(g_err, sizeof g_err, "%s", msg); }
+
+namespace {
 
 // ------------------------------------------------------------------ timing
 enum { kIdCoef = 0, kIdScore, kIdSelect, kIdCompact, kIdCalib, kNumIds };

@@ -1,0 +1,242 @@
+"""TRIA statistics files and the two scalings applied to loaded statistics (host
+code of the library, no GPU).
+
+Pins:
+* the facts the pages state (tests/golden/stats_files.json): the magic, the
+  versions 1..3, the header of the v2 file a loader log line reports
+  (24 layers, 8 heads, 2 KV heads, fc 128), the record fields with mrl
+  skippable, layer budget scales defaulting to 1.0;
+* the byte layout (a reading: the pages give neither the byte order nor the field
+  order) against a writer of its own here, built with ``struct``, so that the C
+  parser and encoder are each checked against code they do not share;
+* the band mask against the oracle: scaling band f's centre by m_f scales band f's
+  offset-averaged trigonometric term by m_f and leaves the norm term unchanged
+  [Fold note, sec. 7: an offset-independent per-band rescaling multiplies
+  ||mu'_f|| and commutes with the fold], checked with the literal 17-offset
+  average, band by band;
+* per-layer budgets: round(budget * scale), half up, with scale 1.0 the uniform
+  budget.
+"""
+import json
+import os
+import struct
+
+import numpy as np
+import pytest
+
+from oracle import tria_oracle as o
+from key_importance_scoring_amd import _lib as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stats_files.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _arrays(nl, nh, fc, seed=0):
+    rng = np.random.default_rng(seed)
+    return tuple(rng.standard_normal((nl, nh, fc)).astype(np.float32) for _ in range(4))
+
+
+def _reference_file(version, nl, nh, nkv, fc, re, im, ab, mrl, scales=None):
+    """A stats file written field by field with struct (little-endian)."""
+    out = [struct.pack("<6I", _golden()["loader"]["magic"], version, nl, nh, nkv, fc)]
+    if version >= 2:
+        out.append(struct.pack("<I", 2 * fc))
+    if version >= 3:
+        out.append(struct.pack("<I", 1 if scales is not None else 0))
+        if scales is not None:
+            out.append(struct.pack(f"<{nl}f", *scales))
+    for l in range(nl):
+        for h in range(nh):
+            for arr in (re, im, ab) + ((mrl,) if version >= 2 else ()):
+                out.append(struct.pack(f"<{fc}f", *arr[l, h]))
+    return b"".join(out)
+
+
+# ----------------------------------------------------------------------------- the file format
+
+def test_golden_facts():
+    g = _golden()
+    assert g["loader"]["magic"] == int(g["loader"]["magic_hex"], 16)
+    # the magic's bytes are the ASCII letters of the format's name, most significant first
+    assert struct.pack(">I", g["loader"]["magic"]) == b"TRIA"
+
+
+@pytest.mark.parametrize("version", [1, 2, 3])
+def test_encoder_matches_reference_writer(version):
+    re, im, ab, mrl = _arrays(3, 4, 8)
+    scales = np.array([1.0, 0.5, 1.25], np.float32) if version == 3 else None
+    mine = L.tria_stats_encode(version, 2, re, im, ab, mrl if version >= 2 else None, scales)
+    ref = _reference_file(version, 3, 4, 2, 8, re, im, ab, mrl, scales)
+    assert mine == ref
+
+
+@pytest.mark.parametrize("version,with_scales", [(1, False), (2, False), (3, False), (3, True)])
+def test_parse_reference_file(version, with_scales):
+    re, im, ab, mrl = _arrays(2, 6, 16, seed=version)
+    scales = np.array([0.75, 1.5], np.float32) if with_scales else None
+    info, r2, i2, a2, m2, s2 = L.tria_stats_parse(_reference_file(version, 2, 6, 3, 16, re, im, ab, mrl, scales))
+    assert (info.version, info.n_layers, info.n_heads, info.n_kv_heads, info.fc, info.head_dim) == \
+        (version, 2, 6, 3, 16, 32)
+    assert info.has_budget_scales == int(with_scales)
+    assert info.mrl_present == int(version >= 2)
+    np.testing.assert_array_equal(r2, re)
+    np.testing.assert_array_equal(i2, im)
+    np.testing.assert_array_equal(a2, ab)
+    np.testing.assert_array_equal(m2, mrl if version >= 2 else np.zeros_like(mrl))
+    want = scales if with_scales else np.full(2, _golden()["record_fields"]["default_layer_budget_scale"])
+    np.testing.assert_array_equal(s2, want)
+
+
+def test_log_line_header():
+    """The v2 file of the loader log in the pages: 24 layers, 8 heads, 2 KV heads,
+    fc 128 (head_dim 256)."""
+    g = _golden()["v2_log_line"]
+    nl, nh, nkv, fc = g["n_layers"], g["n_heads"], g["n_kv_heads"], g["fc"]
+    re, im, ab, mrl = _arrays(nl, nh, fc, seed=11)
+    data = L.tria_stats_encode(g["version"], nkv, re, im, ab, None)
+    # header 7 u32, then 4 records of fc floats per (layer, head)
+    assert len(data) == 7 * 4 + nl * nh * 4 * fc * 4
+    info, r2, _, _, m2, s2 = L.tria_stats_parse(data)
+    assert (info.version, info.n_layers, info.n_heads, info.n_kv_heads, info.fc, info.head_dim) == \
+        (2, 24, 8, 2, 128, 256)
+    np.testing.assert_array_equal(r2, re)
+    assert not m2.any()                  # mrl written as zeros when not given
+    assert (s2 == 1.0).all()
+
+
+def _status(data):
+    with pytest.raises(L.TriaError) as e:
+        L.tria_stats_parse(data)
+    return e.value.status
+
+
+def test_parse_errors():
+    re, im, ab, mrl = _arrays(2, 4, 8)
+    good = _reference_file(3, 2, 4, 2, 8, re, im, ab, mrl, [1.0, 1.0])
+    assert L.tria_stats_parse(good)[0].version == 3
+    assert _status(b"") == L.TRIA_ESHAPE
+    assert _status(good[:20]) == L.TRIA_ESHAPE
+    assert _status(good[:-1]) == L.TRIA_ESHAPE                                # truncated
+    assert _status(good + b"\0") == L.TRIA_ESHAPE                             # trailing bytes
+    assert good[:4] == b"AIRT"                                                 # the magic, little-endian
+    assert _status(b"TRIA" + good[4:]) == L.TRIA_EINVAL                        # the magic, big-endian
+    for v in (0, 4):
+        assert _status(good[:4] + struct.pack("<I", v) + good[8:]) == L.TRIA_EINVAL
+    # head_dim != 2 fc
+    assert _status(good[:24] + struct.pack("<I", 15) + good[28:]) == L.TRIA_ESHAPE
+    # an unknown flag bit
+    assert _status(good[:28] + struct.pack("<I", 3) + good[32:]) == L.TRIA_EINVAL
+    # query heads not a multiple of KV heads
+    assert _status(good[:16] + struct.pack("<I", 3) + good[20:]) == L.TRIA_ESHAPE
+    # zero layers
+    assert _status(good[:8] + struct.pack("<I", 0) + good[12:]) == L.TRIA_ESHAPE
+
+
+def test_encode_rejects_bad_header():
+    re, im, ab, _ = _arrays(1, 3, 4)
+    with pytest.raises(L.TriaError):
+        L.tria_stats_encode(2, 2, re, im, ab)                # 3 query heads over 2 KV heads
+    with pytest.raises(L.TriaError):
+        L.tria_stats_encode(4, 1, re, im, ab)
+
+
+# ----------------------------------------------------------------------------- band mask
+
+def _band_terms(mu, absm, k, dist, offsets, omega):
+    """Per band: the literal offset-averaged trigonometric term of that band alone."""
+    F = mu.size
+    out = np.empty((F, k.shape[0]))
+    for f in range(F):
+        one = np.zeros(F, complex)
+        one[f] = mu[f]
+        out[f] = o.s_trig_direct(one, k, dist, offsets, omega)
+    return out
+
+
+def test_band_mask_scales_each_band_and_keeps_norm():
+    d, theta = 32, 1e6
+    F = d // 2
+    offsets = [2 ** i for i in range(17)]
+    omega = o.band_frequencies(d, theta)
+    rng = np.random.default_rng(3)
+    re, im = (rng.standard_normal((2, 3, F)).astype(np.float32) for _ in range(2))
+    ab = (np.hypot(re, im) * rng.uniform(1.0, 1.5, (2, 3, F))).astype(np.float32)
+    mask = rng.uniform(0.0, 2.0, F).astype(np.float32)
+    mask[[0, 3]] = 0.0                                 # masked out
+    mask[5] = 1.0                                      # unchanged
+    r2, i2, a2 = re.copy(), im.copy(), ab.copy()
+    L.tria_stats_band_mask(mask, r2, i2, a2)
+    # a band with mask 1 is untouched bit for bit; a band with mask 0 has no centre
+    for x, y in ((r2, re), (i2, im), (a2, ab)):
+        np.testing.assert_array_equal(x[..., 5], y[..., 5])
+    assert not r2[..., [0, 3]].any() and not i2[..., [0, 3]].any()
+    k = rng.standard_normal((40, F)) + 1j * rng.standard_normal((40, F))
+    dist = rng.integers(0, 5000, 40).astype(np.float64)
+    for l in range(2):
+        for h in range(3):
+            mu = re[l, h].astype(np.float64) + 1j * im[l, h]
+            mu_m = r2[l, h].astype(np.float64) + 1j * i2[l, h]
+            per_band = _band_terms(mu, ab[l, h], k, dist, offsets, omega)
+            want = mask.astype(np.float64) @ per_band
+            got = o.s_trig_direct(mu_m, k, dist, offsets, omega)
+            scale = np.abs(per_band).sum(axis=0) * mask.max()
+            np.testing.assert_array_less(np.abs(got - want), 1e-6 * scale + 1e-12)
+            n0 = o.s_norm(mu, ab[l, h].astype(np.float64), k)
+            n1 = o.s_norm(mu_m, a2[l, h].astype(np.float64), k)
+            np.testing.assert_array_less(np.abs(n1 - n0), 1e-6 * (np.abs(k) @ ab[l, h]) * (1 + mask.max()))
+
+
+def test_band_mask_argument_errors():
+    re, im, ab, _ = _arrays(1, 2, 4)
+    with pytest.raises(ValueError):
+        L.tria_stats_band_mask(np.ones(3, np.float32), re, im, ab)
+    with pytest.raises(L.TriaError):
+        L.tria_stats_band_mask(np.array([1, -1, 1, 1], np.float32), re, im, ab)
+    with pytest.raises(L.TriaError):
+        L.tria_stats_band_mask(np.array([1, np.nan, 1, 1], np.float32), re, im, ab)
+    with pytest.raises(TypeError):
+        L.tria_stats_band_mask(np.ones(4, np.float32), re.astype(np.float64), im, ab)
+
+
+# ----------------------------------------------------------------------------- per-layer budgets
+
+def test_layer_budgets():
+    scales = np.array([1.0, 0.5, 0.25, 1.5, 0.0], np.float32)
+    layer = np.array([0, 1, 2, 3, 4, 1, 0], np.int32)
+    b = L.tria_stats_layer_budgets(layer, scales, 2049)
+    # 2049 * 0.5 = 1024.5 -> 1025 (half up); 2049 * 0.25 = 512.25 -> 512; 2049 * 1.5 = 3073.5 -> 3074
+    np.testing.assert_array_equal(b, [2049, 1025, 512, 3074, 0, 1025, 2049])
+    np.testing.assert_array_equal(L.tria_stats_layer_budgets(layer, np.ones(5, np.float32), 77), np.full(7, 77))
+    assert L.tria_stats_layer_budgets(np.zeros(0, np.int32), scales, 5).size == 0
+    with pytest.raises(L.TriaError):
+        L.tria_stats_layer_budgets(np.array([5], np.int32), scales, 10)
+    with pytest.raises(L.TriaError):
+        L.tria_stats_layer_budgets(np.array([0], np.int32), np.array([-1.0], np.float32), 10)
+
+
+# ----------------------------------------------------------------------------- file helpers
+
+def test_save_load_files(tmp_path):
+    from key_importance_scoring_amd import stats
+    re, im, ab, mrl = _arrays(4, 8, 32, seed=9)
+    p = str(tmp_path / "stats.bin")
+    n = stats.save(p, 2, re, im, ab, mrl, layer_budget_scales=[1.0, 0.5, 0.5, 2.0])
+    assert os.path.getsize(p) == n
+    s = stats.load(p)
+    assert s.version == 3 and s.n_kv_heads == 2 and s.shape == (4, 8, 32)
+    np.testing.assert_array_equal(s.mrl, mrl)
+    np.testing.assert_array_equal(s.unit_budgets([0, 1, 2, 3], 100), [100, 50, 50, 200])
+    mask = np.linspace(0.0, 1.0, 32, dtype=np.float32)
+    m = stats.load(p, band_mask=mask)
+    np.testing.assert_allclose(m.q_mean_re, re * mask, rtol=1e-6, atol=0)
+    # the norm weight E|q| - |E q| is what it was
+    np.testing.assert_allclose(m.q_abs_mean - np.hypot(m.q_mean_re, m.q_mean_im), ab - np.hypot(re, im),
+                               rtol=0, atol=1e-5)
+    p1 = str(tmp_path / "v1.bin")
+    stats.save(p1, 8, re, im, ab, version=1)
+    s1 = stats.load(p1)
+    assert s1.version == 1 and not s1.mrl.any() and (s1.layer_budget_scales == 1.0).all()
