@@ -380,6 +380,8 @@ def main() -> int:
                     help="instead of the single pass, time the decode loop (append 128 tokens, prune in place)")
     ap.add_argument("--offsets", choices=("mean", "max"), default="mean",
                     help="reduction over the future offsets: the mean (the method) or the maximum variant")
+    ap.add_argument("--select", choices=("auto", "per_group", "tiled"), default="auto",
+                    help="tria_select's work distribution (auto: the library's default)")
     args = ap.parse_args()
     # a calibration step is ~0.4 ms: more of them keep the timed region near 0.1 s
     if args.steps is None:
@@ -423,6 +425,8 @@ def main() -> int:
     prob = DeviceProblem(cfg, device="cuda:0", keep_raw=False, k_host=hosts.get("k"), v_host=hosts.get("v"))
     hosts.clear()
     stream = torch.cuda.current_stream()
+    L.tria_select_strategy({"auto": L.SELECT_AUTO, "per_group": L.SELECT_PER_GROUP,
+                            "tiled": L.SELECT_TILED}[args.select])
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         prob.run(stream)
@@ -488,7 +492,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": workload_desc(cfg),
+        "config": dict(workload_desc(cfg), **({"select": args.select} if args.select != "auto" else {})),
         "hbm_algorithmic_GBps": alg / (ms / 1e3) / 1e9,
         "hbm_pct_of_peak": 100.0 * alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": alg,

@@ -149,7 +149,7 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 
 // ------------------------------------------------------------------ workspace
 struct Layout {
-  size_t B, Bmax, part, claim, hist, st, tiles, list, total;
+  size_t B, Bmax, part, claim, hist, st, tiles, list, masks, total;
   int32_t n_tiles, n_st;
   tria::OffsetBlocks ob;
 };
@@ -158,7 +158,7 @@ size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace: [flag word | MFMA B operands | (maximum over offsets) offset-block B
 // operands | tile moments | tile claim counter | aggregate histograms | selection
-// state | per-tile counts | candidates]
+// state | per-tile counts | candidates | per-tile slot masks]
 Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   Layout L{};
   const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
@@ -186,6 +186,8 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   off += al256(ug * (size_t)L.n_st * 4 * 4);  // above-b1 counts, offsets, tie shares, candidates
   L.list = off;
   off += al256(ug * (size_t)n_max * 4);
+  L.masks = off;  // per tile and thread: slots above the threshold bin, slots in it
+  off += al256(ug * (size_t)L.n_st * 256 * sizeof(tria::SelMask) * 2);
   L.total = off;
   return L;
 }
@@ -285,8 +287,9 @@ tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, in
   const size_t nt = (size_t)n_units * p->n_kv_heads * L.n_st;
   tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, L.n_st, len, budget, agg,
                       reinterpret_cast<const uint32_t*>(w + L.hist), reinterpret_cast<tria::SelState*>(w + L.st),
-                      tiles, tiles + nt, tiles + 2 * nt, tiles + 3 * nt, reinterpret_cast<int32_t*>(w + L.list), idx,
-                      cnt,
+                      tiles, tiles + nt, tiles + 2 * nt, tiles + 3 * nt, reinterpret_cast<int32_t*>(w + L.list),
+                      reinterpret_cast<tria::SelMask*>(w + L.masks),
+                      reinterpret_cast<tria::SelMask*>(w + L.masks) + nt * 256, idx, cnt,
                       reinterpret_cast<int32_t*>(w)};
   const int strategy = g_select_strategy.load();
   hipError_t e = timed(kIdSelect, s, [&] { return tria::launch_select(sa, strategy, s); });

@@ -2,6 +2,8 @@
 // (tria_kernels.hip).  Not installed; the public interface is include/tria.h.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,6 +129,11 @@ constexpr int kSelGroupMax = 32768;     // per-group selection: 512 threads x 64
 constexpr int kRefineLds = 3072;        // candidates the refinement keeps in LDS
 constexpr int kMaxSelTiles = 2048;      // per (unit, KV head): n_max <= 2048 kSelTile
 
+// A selection tile's per-thread bit masks: bit k stands for slot s0 + k of the
+// thread's kSelTile / 256 consecutive slots.
+using SelMask = std::conditional<(kSelTile / 256 <= 8), uint8_t,
+                                 std::conditional<(kSelTile / 256 <= 16), uint16_t, uint32_t>::type>::type;
+
 struct SelectArgs {
   int32_t n_units, n_max, b_max, hkv, sink, window, n_st;
   const int32_t* len;
@@ -139,6 +146,8 @@ struct SelectArgs {
   int32_t* tile_eqb;          // [U][Hkv][n_st] tied slots kept per tile
   int32_t* tile_m;            // [U][Hkv][n_st] candidates (slots of bin b1) per tile
   int32_t* list;              // [U][Hkv][n_max] candidate slots, tile j's from j * kSelTile
+  SelMask* gmask;             // [U][Hkv][n_st][256] per thread: slots above b1
+  SelMask* cmask;             // [U][Hkv][n_st][256] per thread: slots of bin b1 (candidates)
   int32_t* idx;               // [U][Hkv][b_max]
   int32_t* cnt;               // [U]
   int32_t* flags;

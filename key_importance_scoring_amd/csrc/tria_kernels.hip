@@ -1086,16 +1086,20 @@ __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   float x[kSelSpt];
   load_slots(a.agg + (size_t)ug * a.n_max, s0, a.n_max, x);
   const SelState bd = a.st[ug];
-  uint32_t cgt = 0, cm = 0;
+  uint32_t gm = 0, cmk = 0;   // per-slot bits: above b1, in b1
 #pragma unroll
   for (int k = 0; k < kSelSpt; ++k) {
     if (s0 + k < bd.n) {
       const int bin = lin_bin(x[k]);
-      cgt += bin > bd.b1 ? 1u : 0u;
-      cm += bin == bd.b1 ? 1u : 0u;
+      gm |= (bin > bd.b1 ? 1u : 0u) << k;
+      cmk |= (bin == bd.b1 ? 1u : 0u) << k;
     }
   }
-  const uint32_t gt_tot = block_scan_incl<256>(cgt, wtot);
+  // the masks, for k_sel_emit (which then reads the aggregates of candidates only)
+  a.gmask[(size_t)blockIdx.x * 256 + tid] = (SelMask)gm;
+  a.cmask[(size_t)blockIdx.x * 256 + tid] = (SelMask)cmk;
+  const uint32_t cm = (uint32_t)__popc(cmk);
+  const uint32_t gt_tot = block_scan_incl<256>((uint32_t)__popc(gm), wtot);
   const uint32_t m_incl = block_scan_incl<256>(cm, wtot);
   if (tid == 255) {
     a.tile_gt[blockIdx.x] = (int32_t)gt_tot;
@@ -1106,9 +1110,7 @@ __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   if (cm) {
     int32_t* list = a.list + (size_t)ug * a.n_max + (size_t)j * kSelTile;
     uint32_t pos = m_incl - cm;
-#pragma unroll
-    for (int k = 0; k < kSelSpt; ++k)
-      if (s0 + k < bd.n && lin_bin(x[k]) == bd.b1) list[pos++] = s0 + k;
+    for (uint32_t m = cmk; m; m &= m - 1) list[pos++] = s0 + __ffs(m) - 1;
   }
 }
 
@@ -1251,27 +1253,24 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
   const int tid = threadIdx.x;
   __shared__ uint32_t wtot[4];
-  // every load at once: the tile's aggregates (clamped inside the row), the group's
-  // state and the tile's offset and tie share
+  // every load at once: the thread's masks from k_sel_collect, the group's state and
+  // the tile's offset and tie share
   const int s0 = (blockIdx.x % a.n_st) * kSelTile + kSelSpt * tid;
-  float x[kSelSpt];
-  load_slots(a.agg + (size_t)ug * a.n_max, s0, a.n_max, x);
+  uint32_t gtm = a.gmask[(size_t)blockIdx.x * 256 + tid];   // above b1: kept
+  const uint32_t cm = a.cmask[(size_t)blockIdx.x * 256 + tid];
   const SelState st = a.st[ug];
   const uint32_t eqb = (uint32_t)a.tile_eqb[blockIdx.x];
   const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
   const uint32_t T = (uint32_t)st.T;
-  uint32_t gtm = 0, eqm = 0;   // per-slot bit masks
-  {
-#pragma unroll
-    for (int k = 0; k < kSelSpt; ++k) {
-      if (s0 + k < st.n) {
-        const int bin = lin_bin(x[k]);
-        const uint32_t key = order_key(x[k]);
-        const bool gt = bin > st.b1 || (bin == st.b1 && key > T);
-        const bool eq = bin == st.b1 && key == T;
-        gtm |= (gt ? 1u : 0u) << k;
-        eqm |= (eq ? 1u : 0u) << k;
-      }
+  // candidates (slots of bin b1): above the threshold key T kept, equal to T tied
+  uint32_t eqm = 0;
+  if (cm) {
+    const float* row = a.agg + (size_t)ug * a.n_max;
+    for (uint32_t m = cm; m; m &= m - 1) {
+      const int k = __ffs(m) - 1;
+      const uint32_t key = order_key(row[s0 + k]);
+      gtm |= (key > T ? 1u : 0u) << k;
+      eqm |= (key == T ? 1u : 0u) << k;
     }
   }
   // tied slots of this tile are kept lowest first, up to its share eqb
