@@ -200,6 +200,45 @@ def test_zero_statistics_break_ties_by_slot(strategy):
     _check_oracle_compaction(prob, kept)
 
 
+def test_duplicate_rows_tie_rule(strategy):
+    """Keys that repeat every 97 slots score identically (a cached row's score
+    depends on the row only), so the aggregates hold many exact ties around the
+    threshold: every slot above the kept set's smallest candidate aggregate T is
+    kept, none below it, and the tied slots kept are the lowest ones.  Checked on
+    the GPU's own aggregates, and the strategies must agree bit for bit."""
+    cfg = C["qwen3_8b"].replace(name="dup_rows", n_layers=1, n_kv_heads=2, n_kv=4000, budget=1000)
+    prob = DeviceProblem(cfg)
+    assert prob.paging is None
+    idx = torch.arange(prob.K.shape[2], device=prob.K.device) % 97
+    prob.K.copy_(prob.K[:, :, idx])
+    prob.run()
+    torch.cuda.synchronize()
+    assert prob.flags() == 0
+    n, B = int(synth.units(cfg).lengths[0]), int(synth.units(cfg).budget[0])
+    prot = o.protected_mask(n, cfg.sink, cfg.window)
+    for g in range(cfg.n_kv_heads):
+        agg = prob.agg[0, g, :n].cpu().numpy()
+        kept = prob.kept(0, g)
+        assert kept.size == min(B, n)
+        mask = np.zeros(n, bool)
+        mask[kept] = True
+        assert mask[prot].all()
+        T = agg[mask & ~prot].min()
+        assert mask[agg > T].all() and not mask[agg < T].any()
+        tied = np.nonzero(agg == T)[0]
+        n_tied_kept = int(mask[tied].sum())
+        assert 1 <= n_tied_kept < tied.size, "the case should split a tie"
+        np.testing.assert_array_equal(np.nonzero(mask[tied])[0], np.arange(n_tied_kept))
+    ref_idx, ref_cnt = prob.idx.clone(), prob.cnt.clone()
+    prev = L.tria_select_strategy(L.SELECT_PER_GROUP if strategy != L.SELECT_PER_GROUP else L.SELECT_TILED)
+    try:
+        prob.select()
+        torch.cuda.synchronize()
+        assert torch.equal(prob.idx, ref_idx) and torch.equal(prob.cnt, ref_cnt)
+    finally:
+        L.tria_select_strategy(prev)
+
+
 def test_empty_and_zero_budget_units(strategy):
     cfg = C["batched_decode"].replace(name="empty", n_seqs=4, n_kv=700, ragged_min=100, window=0, sink=0)
     prob = DeviceProblem(cfg)
