@@ -614,12 +614,15 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
         for (int b = 0; b < NBI; ++b)
           acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[b][i]), bcur[i], acc[b], 0,
                                                            0, 0);
+      // hi + lo of each (offset, head) into lanes 8..15, then the running maximum
+      // (IEEE maximum: one instruction, where fmaxf would first canonicalise the
+      // running value in every block)
 #pragma unroll
       for (int b = 0; b < NBI; ++b)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[b][t]), 0x118, 0xF, 0xF, true);
-          best[b][t] = fmaxf(best[b][t], acc[b][t] + __int_as_float(other));
+          best[b][t] = __builtin_elementwise_maximum(best[b][t], acc[b][t] + __int_as_float(other));
         }
 #pragma unroll
       for (int i = 0; i < S::NKC; ++i) bcur[i] = bnext[i];
@@ -635,7 +638,7 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
           const int y = sft == 1 ? __builtin_amdgcn_mov_dpp(x, 0x101, 0xF, 0xF, true)
                       : sft == 2 ? __builtin_amdgcn_mov_dpp(x, 0x102, 0xF, 0xF, true)
                                  : __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);
-          best[b][t] = fmaxf(best[b][t], __int_as_float(y));
+          best[b][t] = __builtin_elementwise_maximum(best[b][t], __int_as_float(y));
         }
     }
 #pragma unroll
