@@ -34,6 +34,8 @@
 // per-(unit, query head) coefficient vector.
 #include "tria_kernels.h"
 
+#include <algorithm>
+
 namespace tria {
 namespace {
 
@@ -147,6 +149,17 @@ __device__ inline int lane_band(int q, int c) {
 // order its lanes load them (the MFMA operand layout above).  The block also
 // resets its (unit, KV head)'s tile moments to kUnpublished and clears its
 // aggregate histogram; block (0, 0) clears the tile claim counter.
+// sin and cos of an fp64 angle: reduced modulo 2 pi in fp64, then the fp32 sine and
+// cosine of the remainder (|error| ~1e-7, far below the ~2^-17 relative precision of
+// the split bf16 operands the coefficients end up in).
+__device__ inline void sincos_reduced(double ang, double* sv, double* cv) {
+  const float r = (float)(ang - 6.283185307179586 * rint(ang * 0.15915494309189535));
+  float s, c;
+  sincosf(r, &s, &c);
+  *sv = s;
+  *cv = c;
+}
+
 template <int D, int P>
 __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   using S = Shape<D>;
@@ -163,20 +176,25 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   __shared__ float s_n[kMaxGroup * F];  // norm weights
   __shared__ double s_mur[kMaxGroup * F], s_mui[kMaxGroup * F], s_w[F];  // maximum over offsets
 
+  // blockIdx.z > 0 (the maximum over offsets only) writes a share of the offset
+  // blocks' operands and nothing else
+  const bool first = blockIdx.z == 0;
   // tiles past len[u] hold no keys: their moments are published here, as zeros
-  const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
-  const int64_t per = (int64_t)G * a.n_tiles * 3;
-  for (int64_t i = t; i < per; i += 256) {
-    const int tile = (int)((i / 3) % a.n_tiles);
-    a.part[ug * per + i] = (int64_t)tile * a.tile >= n_u ? 0ull : kUnpublished;
+  if (first) {
+    const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
+    const int64_t per = (int64_t)G * a.n_tiles * 3;
+    for (int64_t i = t; i < per; i += 256) {
+      const int tile = (int)((i / 3) % a.n_tiles);
+      a.part[ug * per + i] = (int64_t)tile * a.tile >= n_u ? 0ull : kUnpublished;
+    }
+    for (int i = t; i < kBins; i += 256) a.hist[ug * kBins + i] = 0u;
+    if (u == 0 && g == 0 && t == 0) *a.next_tile = 0;
   }
-  for (int i = t; i < kBins; i += 256) a.hist[ug * kBins + i] = 0u;
-  if (u == 0 && g == 0 && t == 0) *a.next_tile = 0;
 
   // statistics of this thread's (query head, band) pairs, loaded while the twiddles are formed
   const int layer = a.unit_layer[u];
   const bool ok = layer >= 0 && layer < a.layers;
-  if (!ok && t == 0 && g == 0) raise_flag(a.flags, kFlagLayer);
+  if (!ok && t == 0 && g == 0 && first) raise_flag(a.flags, kFlagLayer);
   double mr[PER], mi[PER], ab[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
@@ -197,7 +215,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   double cs = 0.0, sn = 0.0;
   for (int j = sub; j < offs.n; j += subs) {
     double sv, cv;
-    sincos(w * offs.v[j], &sv, &cv);
+    sincos_reduced(w * offs.v[j], &sv, &cv);
     cs += cv;
     sn += sv;
   }
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     wr /= offs.n;  // W_f  [Fold note, Eq. 6]
     wi /= offs.n;
     double sv, cv;
-    sincos(w * (double)a.q_pos[u], &sv, &cv);
+    sincos_reduced(w * (double)a.q_pos[u], &sv, &cv);
     rot_re[t] = wr * cv - wi * sv;  // W_f e^{i w_f q_pos}
     rot_im[t] = wr * sv + wi * cv;
   }
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   // B operands: operand s of lane l at B[(u, g)][s][l]; s < NKC are the dot part's
   // chunks, then the norm part's hi-magnitude and lo-magnitude operands
   u32x4* dst = reinterpret_cast<u32x4*>(a.B) + ug * NB * 64;
-  for (int q = t; q < NB * 64; q += 256) {
+  for (int q = first ? t : NB * 64; q < NB * 64; q += 256) {
     const int s = q / 64, lane = q % 64;
     const int col = lane & 15, grp = lane >> 4;
     int head = -1;
@@ -287,7 +305,9 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     const double qp = (double)a.q_pos[u];
     u32x4* dstm = reinterpret_cast<u32x4*>(a.Bmax) + ug * ob.nblk * S::NKC * 64;
     const int nq = ob.nblk * S::NKC * 64;
-    for (int q = t; q < nq; q += 256) {
+    const int share = (nq + (int)gridDim.z - 1) / (int)gridDim.z;   // this block's operands
+    const int q1 = min(nq, share * ((int)blockIdx.z + 1));
+    for (int q = share * (int)blockIdx.z + t; q < q1; q += 256) {
       const int cb = q / (S::NKC * 64), i = (q / 64) % S::NKC, lane = q % 64;
       const int col = lane & 15, grp = lane >> 4, j = col & 7;
       const bool lo = col >= 8;
@@ -1804,7 +1824,13 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
 // ============================================================================ launches
 hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   if (a.n_units == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_units, (unsigned)a.hkv);
+  // the maximum over offsets writes nblk * d/32 * 64 operands per (unit, KV head):
+  // with few pairs, they are shared out over up to nblk blocks per pair so that the
+  // launch fills the device
+  const long pairs = (long)a.n_units * a.hkv;
+  int zs = 1;
+  if (a.omax) zs = (int)std::max(1L, std::min<long>(a.ob.nblk, (1024 + pairs - 1) / pairs));
+  const dim3 grid((unsigned)a.n_units, (unsigned)a.hkv, (unsigned)zs);
 #define TRIA_COEF_CASE(DD, PP)                                                   \
   if (a.d == DD && a.pairing == PP) {                                           \
     hipLaunchKernelGGL((k_coef<DD, PP>), grid, dim3(256), 0, s, a, offs);       \
