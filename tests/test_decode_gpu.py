@@ -46,18 +46,17 @@ def _stats(cfg):
     return re.astype(np.float64) + 1j * im.astype(np.float64), ab.astype(np.float64)
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_decode_loop_matches_oracle_loop(name):
-    cfg, budget, interval, steps = CASES[name]
-    log(f"[decode] {name}: seqs={cfg.n_units} Hkv={cfg.n_kv_heads} G={cfg.group} d={cfg.head_dim} "
-        f"budget={budget} interval={interval} bs={cfg.block_size} reduce={cfg.offset_reduce}")
-    loop = DecodeLoop(cfg, budget, interval)
+def _drive(loop, cfg, budget, interval, steps, pairs, name):
+    """Runs the loop for `steps` appends and, after every prune, checks the
+    (sequence, KV head) pairs in `pairs` against the oracle loop; returns the number
+    of prunes checked."""
     mu, absm = _stats(cfg)
     layer = synth.units(cfg).unit_layer
     G = cfg.group
     # oracle state per (sequence, KV head): positions, K bits, V bits
     st = {(u, g): (np.zeros(0, np.int64), np.zeros((0, cfg.head_dim), np.uint16),
-                   np.zeros((0, cfg.head_dim), np.uint16)) for u in range(cfg.n_units) for g in range(cfg.n_kv_heads)}
+                   np.zeros((0, cfg.head_dim), np.uint16)) for u, g in pairs}
+    checked = 0
     for step in range(steps):
         kn, vn, pn = loop.new_rows(interval)
         for (u, g), (ps, ks, vs) in st.items():
@@ -67,28 +66,27 @@ def test_decode_loop_matches_oracle_loop(name):
         assert loop.flags() == 0
         if not pruned:
             continue
+        checked += 1
         q_pos = int(loop.next_pos[0] - 1)
         agg = loop.agg.cpu().numpy()
         idx = loop.idx.cpu().numpy()
         cnt = loop.cnt.cpu().numpy()
-        for u in range(cfg.n_units):
-            for g in range(cfg.n_kv_heads):
-                ps, ks, vs = st[(u, g)]
-                n = ps.size
-                what = f"{name} step {step} seq {u} kv {g}"
-                rows = o.bf16_bits_to_f64(ks)
-                raw = np.stack([o.score_head(rows, ps, q_pos, mu[layer[u], h], absm[layer[u], h], cfg.head_dim,
-                                             cfg.pairing, cfg.rope_base, cfg.offsets, "direct", cfg.offset_reduce)
-                                for h in range(g * G, (g + 1) * G)])
-                o_agg = o.aggregate_unit(raw, n, G, cfg.sink, cfg.window, cfg.agg)[0]
-                o_kept = o.select(o_agg, budget)
-                check_agg(agg[u, g, :n], o_agg, what)
-                k = int(cnt[u])
-                assert k == min(budget, n), what
-                g_kept = idx[u, g, :k].astype(np.int64)
-                check_kept(g_kept, o_kept, o_agg, n, budget, cfg.sink, cfg.window, what)
-                # both continue from the GPU's kept set
-                st[(u, g)] = (ps[g_kept], ks[g_kept], vs[g_kept])
+        for (u, g), (ps, ks, vs) in list(st.items()):
+            n = ps.size
+            what = f"{name} step {step} seq {u} kv {g}"
+            rows = o.bf16_bits_to_f64(ks)
+            raw = np.stack([o.score_head(rows, ps, q_pos, mu[layer[u], h], absm[layer[u], h], cfg.head_dim,
+                                         cfg.pairing, cfg.rope_base, cfg.offsets, "direct", cfg.offset_reduce)
+                            for h in range(g * G, (g + 1) * G)])
+            o_agg = o.aggregate_unit(raw, n, G, cfg.sink, cfg.window, cfg.agg)[0]
+            o_kept = o.select(o_agg, budget)
+            check_agg(agg[u, g, :n], o_agg, what)
+            k = int(cnt[u])
+            assert k == min(budget, n), what
+            g_kept = idx[u, g, :k].astype(np.int64)
+            check_kept(g_kept, o_kept, o_agg, n, budget, cfg.sink, cfg.window, what)
+            # both continue from the GPU's kept set
+            st[(u, g)] = (ps[g_kept], ks[g_kept], vs[g_kept])
         pos = loop.pos.cpu().numpy()
         for (u, g), (ps, ks, vs) in st.items():
             k = ps.size
@@ -96,7 +94,36 @@ def test_decode_loop_matches_oracle_loop(name):
             np.testing.assert_array_equal(pos[u, g, :k], ps, err_msg=what)
             np.testing.assert_array_equal(loop.head_rows("k", u, g, k), ks, err_msg=what)
             np.testing.assert_array_equal(loop.head_rows("v", u, g, k), vs, err_msg=what)
-    assert loop.prunes >= 2
+        # every pair: the kept count, ascending positions, the window's newest slots kept
+        for u in range(cfg.n_units):
+            k = int(cnt[u])
+            assert k == min(budget, int(loop.len_host[u]))
+            for g in range(cfg.n_kv_heads):
+                assert (np.diff(pos[u, g, :k]) > 0).all(), (name, step, u, g)
+                assert pos[u, g, k - 1] == loop.next_pos[u] - 1
+    return checked
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_loop_matches_oracle_loop(name):
+    cfg, budget, interval, steps = CASES[name]
+    log(f"[decode] {name}: seqs={cfg.n_units} Hkv={cfg.n_kv_heads} G={cfg.group} d={cfg.head_dim} "
+        f"budget={budget} interval={interval} bs={cfg.block_size} reduce={cfg.offset_reduce}")
+    loop = DecodeLoop(cfg, budget, interval)
+    pairs = [(u, g) for u in range(cfg.n_units) for g in range(cfg.n_kv_heads)]
+    assert _drive(loop, cfg, budget, interval, steps, pairs, name) >= 2
+
+
+def test_decode_loop_full_size_sampled():
+    """The benchmark's decode loop (64 sequences x 8 KV heads, d 128, G 4, paged,
+    budget 2048, window 256, sink 0, interval 128) through three prunes: sampled
+    (sequence, KV head) pairs against the oracle loop, properties on every pair."""
+    cfg = C["batched_decode"].replace(name="decode_loop", n_seqs=64, ragged_min=0, window=256, sink=0)
+    budget, interval = 2048, 128
+    log(f"[decode] full size: seqs={cfg.n_units} Hkv={cfg.n_kv_heads} budget={budget}")
+    loop = DecodeLoop(cfg, budget, interval)
+    steps = -(-budget // interval) + 3
+    assert _drive(loop, cfg, budget, interval, steps, [(0, 0), (37, 5), (63, 7)], "decode_full") == 3
 
 
 def test_inplace_matches_out_of_place():
