@@ -324,14 +324,17 @@ typedef struct tria_stats_info {
  * [n_layers][n_heads][fc] floats each (the layout tria_score reads); mrl zeros for
  * version 1; layer_budget_scales [n_layers] (1.0 where the file has none).  Returns
  * TRIA_EINVAL for a wrong magic, version or flag, TRIA_ESHAPE for inconsistent or
- * truncated data (the size must match the header exactly). */
+ * truncated data (the size must match the header exactly) or a header beyond 65536
+ * layers, 4096 query heads or 4096 bands.  With all arrays NULL it reads the header
+ * only; *info is written only on success.  The message is in tria_last_error(). */
 tria_status tria_stats_parse(const void* bytes, size_t n_bytes, tria_stats_info* info, float* q_mean_re,
                              float* q_mean_im, float* q_abs_mean, float* mrl, float* layer_budget_scales);
 
 /* Writes a stats file of info->version into out (cap bytes) and returns its size;
  * with out NULL or cap too small it writes nothing and returns the size needed; 0
- * for invalid arguments.  mrl may be NULL (zeros); layer_budget_scales is written
- * for version 3 when info->has_budget_scales is set. */
+ * for invalid arguments (as the parser: at most 65536 layers, 4096 query heads,
+ * 4096 bands).  mrl may be NULL (zeros); layer_budget_scales is written for
+ * version 3 when info->has_budget_scales is set. */
 size_t tria_stats_encode(const tria_stats_info* info, const float* q_mean_re, const float* q_mean_im,
                          const float* q_abs_mean, const float* mrl, const float* layer_budget_scales, void* out,
                          size_t cap);

@@ -134,6 +134,8 @@ size_t tria_stats_encode(const tria_stats_info* info, const float* q_mean_re, co
       info->n_kv_heads == 0 || info->fc == 0 || info->n_heads % info->n_kv_heads || !q_mean_re || !q_mean_im ||
       !q_abs_mean)
     return 0;
+  // the sizes the parser accepts
+  if (info->n_layers > (1u << 16) || info->n_heads > (1u << 12) || info->fc > (1u << 12)) return 0;
   const uint32_t flags = (info->version >= 3 && info->has_budget_scales && layer_budget_scales) ? 1u : 0u;
   const size_t need = header_bytes(info->version, flags, info->n_layers) +
                       (size_t)info->n_layers * info->n_heads * record_floats(info->version, info->fc) * 4;

@@ -142,6 +142,9 @@ def test_encode_rejects_bad_header():
         L.tria_stats_encode(2, 2, re, im, ab)                # 3 query heads over 2 KV heads
     with pytest.raises(L.TriaError):
         L.tria_stats_encode(4, 1, re, im, ab)
+    big = np.zeros((1, 1, 4097), np.float32)                # more bands than the parser takes
+    with pytest.raises(L.TriaError):
+        L.tria_stats_encode(2, 1, big, big, big)
 
 
 # ----------------------------------------------------------------------------- band mask
