@@ -35,6 +35,7 @@
 #include "tria_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace tria {
 namespace {
@@ -673,6 +674,85 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     }
   };
 
+  // maximum over offsets, two stages at once: every offset block's B operands are
+  // read from LDS once for both stages' key blocks (the LDS is this mode's busiest
+  // unit); the norm term is formed last, so that its accumulators are not held
+  // across the offset blocks.  TWO = false: the first stage only (a wave's tail).
+  auto compute_max2 = [&](auto two, const Stage<D, MAXO>& c0, const Stage<D, MAXO>& c1, int kb) {
+    constexpr bool TWO = decltype(two)::value;
+    constexpr int NB2 = TWO ? 2 * NBI : NBI;
+    // key block bb of the pair: blocks 0 .. NBI-1 from the first stage, then the second's
+    auto blk = [&](int bb) -> const u32x4 (&)[D / 32] { return bb < NBI ? c0[bb] : c1[bb - NBI]; };
+    f32x4 best[NB2];
+#pragma unroll
+    for (int bb = 0; bb < NB2; ++bb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) best[bb][t] = -__builtin_inff();
+    const int nblk = a.ob.nblk;
+    for (int cb = 0; cb < nblk; ++cb) {
+      bf16x8 bo[S::NKC];
+#pragma unroll
+      for (int i = 0; i < S::NKC; ++i) bo[i] = __builtin_bit_cast(bf16x8, s_bmax[(cb * S::NKC + i) * 64 + lane]);
+      f32x4 acc[NB2];
+#pragma unroll
+      for (int bb = 0; bb < NB2; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < S::NKC; ++i)
+#pragma unroll
+        for (int bb = 0; bb < NB2; ++bb)
+          acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, blk(bb)[i]), bo[i], acc[bb],
+                                                            0, 0, 0);
+      // hi + lo of each (offset, head) into lanes 8..15, then the running maximum
+#pragma unroll
+      for (int bb = 0; bb < NB2; ++bb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[bb][t]), 0x118, 0xF, 0xF, true);
+          best[bb][t] = __builtin_elementwise_maximum(best[bb][t], acc[bb][t] + __int_as_float(other));
+        }
+    }
+    // the offsets held by lanes 8 + q G' + h, q < opb, meet in lane 8 + h
+    for (int sft = a.ob.gp; sft < 8; sft *= 2) {
+#pragma unroll
+      for (int bb = 0; bb < NB2; ++bb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int x = __float_as_int(best[bb][t]);
+          const int y = sft == 1 ? __builtin_amdgcn_mov_dpp(x, 0x101, 0xF, 0xF, true)
+                      : sft == 2 ? __builtin_amdgcn_mov_dpp(x, 0x102, 0xF, 0xF, true)
+                                 : __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);
+          best[bb][t] = __builtin_elementwise_maximum(best[bb][t], __int_as_float(y));
+        }
+    }
+    // the norm term (no offset), hi + lo merged into the owner lanes as well
+#pragma unroll
+    for (int bb = 0; bb < NB2; ++bb) {
+      f32x4 nrm = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < S::NNC; ++i) {
+        u32x4 h4, l4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float m0 = __builtin_amdgcn_sqrtf(band_sq<D, P>(blk(bb), 8 * i + 2 * j));
+          const float m1 = __builtin_amdgcn_sqrtf(band_sq<D, P>(blk(bb), 8 * i + 2 * j + 1));
+          uint32_t hi, lw;
+          split_bf16(m0, m1, hi, lw);
+          h4[j] = hi;
+          l4[j] = lw;
+        }
+        nrm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h4), bna[i], nrm, 0, 0, 0);
+        nrm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l4), bnb[i], nrm, 0, 0, 0);
+      }
+      f32x4 sc;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(nrm[t]), 0x118, 0xF, 0xF, true);
+        sc[t] = best[bb][t] + nrm[t] + __int_as_float(other);
+      }
+      if (owner) *reinterpret_cast<f32x4*>(s_row + kb + 16 * bb + 4 * grp) = sc;
+    }
+  };
+
   // ---- register double buffer over the wave's keys [kw0, kend): the next stage's
   // loads are issued while the current stage computes.  (Keeping two stages in
   // flight across each wait measured slower on the full cache: more outstanding
@@ -681,7 +761,20 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     if constexpr (MAXO) compute_max(ch, kb);
     else compute(ch, kb);
   };
-  if (kw0 < kend) {
+  if constexpr (MAXO) {
+    // the maximum over offsets takes two stages per pass over the offset blocks:
+    // both are loaded (the second issued here, the first at the previous step),
+    // then computed together; the wave's other stage loads follow the compute
+    for (int kb = kw0; kb < kend; kb += 2 * STAGE) {
+      if (kb + STAGE < kend) {
+        load_stage<D, PAGED, MAXO>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
+        compute_max2(std::true_type{}, cA, cB, kb);
+      } else {
+        compute_max2(std::false_type{}, cA, cA, kb);
+      }
+      if (kb + 2 * STAGE < kend) load_stage<D, PAGED, MAXO>(cA, a.k, u, g, kb + 2 * STAGE, kend, col, grp, s_bt, page0);
+    }
+  } else if (kw0 < kend) {
     for (int kb = kw0;; kb += 2 * STAGE) {
       load_stage<D, PAGED, MAXO>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
       compute_stage(cA, kb);
