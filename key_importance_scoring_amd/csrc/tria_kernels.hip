@@ -589,96 +589,11 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     }
   };
 
-  // maximum over offsets: per stage, the norm term once, then every offset block
-  // (MFMA; hi + lo merged into lanes 8..15; in-lane running maximum), then the
-  // offsets a row's lanes hold meet in the owner lane 8 + h of each query head
-  auto compute_max = [&](const Stage<D, MAXO>& ch, int kb) {
-    f32x4 nrm[NBI], best[NBI];
-#pragma unroll
-    for (int b = 0; b < NBI; ++b) {
-      nrm[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < S::NNC; ++i) {
-        u32x4 h4, l4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float m0 = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch[b], 8 * i + 2 * j));
-          const float m1 = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch[b], 8 * i + 2 * j + 1));
-          uint32_t hi, lw;
-          split_bf16(m0, m1, hi, lw);
-          h4[j] = hi;
-          l4[j] = lw;
-        }
-        nrm[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h4), bna[i], nrm[b], 0, 0, 0);
-        nrm[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l4), bnb[i], nrm[b], 0, 0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) best[b][t] = -__builtin_inff();
-    }
-    // blocks in order, the next block's B operands read from LDS while the current
-    // block's MFMAs run; lane 8 + q G' + h keeps the running maximum of head h over
-    // the offsets it holds (the q-th of every block)
-    const int nblk = a.ob.nblk;
-    bf16x8 bcur[S::NKC], bnext[S::NKC];
-#pragma unroll
-    for (int i = 0; i < S::NKC; ++i) bcur[i] = __builtin_bit_cast(bf16x8, s_bmax[i * 64 + lane]);
-    for (int cb = 0; cb < nblk; ++cb) {
-      const int cn = min(cb + 1, nblk - 1);
-#pragma unroll
-      for (int i = 0; i < S::NKC; ++i) bnext[i] = __builtin_bit_cast(bf16x8, s_bmax[(cn * S::NKC + i) * 64 + lane]);
-      f32x4 acc[NBI];
-#pragma unroll
-      for (int b = 0; b < NBI; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < S::NKC; ++i)
-#pragma unroll
-        for (int b = 0; b < NBI; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[b][i]), bcur[i], acc[b], 0,
-                                                           0, 0);
-      // hi + lo of each (offset, head) into lanes 8..15, then the running maximum
-      // (IEEE maximum: one instruction, where fmaxf would first canonicalise the
-      // running value in every block)
-#pragma unroll
-      for (int b = 0; b < NBI; ++b)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[b][t]), 0x118, 0xF, 0xF, true);
-          best[b][t] = __builtin_elementwise_maximum(best[b][t], acc[b][t] + __int_as_float(other));
-        }
-#pragma unroll
-      for (int i = 0; i < S::NKC; ++i) bcur[i] = bnext[i];
-    }
-    // the offsets held by lanes 8 + q G' + h, q < opb, meet in lane 8 + h: row shifts
-    // by G', 2 G', 4 G' (lane l takes lane l + s; lanes past the row are not used)
-    for (int sft = a.ob.gp; sft < 8; sft *= 2) {
-#pragma unroll
-      for (int b = 0; b < NBI; ++b)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int x = __float_as_int(best[b][t]);
-          const int y = sft == 1 ? __builtin_amdgcn_mov_dpp(x, 0x101, 0xF, 0xF, true)
-                      : sft == 2 ? __builtin_amdgcn_mov_dpp(x, 0x102, 0xF, 0xF, true)
-                                 : __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);
-          best[b][t] = __builtin_elementwise_maximum(best[b][t], __int_as_float(y));
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < NBI; ++b) {
-      f32x4 sc;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(nrm[b][t]), 0x118, 0xF, 0xF, true);
-        sc[t] = best[b][t] + nrm[b][t] + __int_as_float(other);
-      }
-      if (owner) *reinterpret_cast<f32x4*>(s_row + kb + 16 * b + 4 * grp) = sc;
-    }
-  };
-
   // maximum over offsets, two stages at once: every offset block's B operands are
   // read from LDS once for both stages' key blocks (the LDS is this mode's busiest
   // unit); the norm term is formed last, so that its accumulators are not held
   // across the offset blocks.  TWO = false: the first stage only (a wave's tail).
-  auto compute_max2 = [&](auto two, const Stage<D, MAXO>& c0, const Stage<D, MAXO>& c1, int kb) {
+  auto compute_max = [&](auto two, const Stage<D, MAXO>& c0, const Stage<D, MAXO>& c1, int kb) {
     constexpr bool TWO = decltype(two)::value;
     constexpr int NB2 = TWO ? 2 * NBI : NBI;
     // key block bb of the pair: blocks 0 .. NBI-1 from the first stage, then the second's
@@ -757,10 +672,6 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
   // loads are issued while the current stage computes.  (Keeping two stages in
   // flight across each wait measured slower on the full cache: more outstanding
   // requests per wave did not raise the delivered bandwidth.)
-  auto compute_stage = [&](const Stage<D, MAXO>& ch, int kb) {
-    if constexpr (MAXO) compute_max(ch, kb);
-    else compute(ch, kb);
-  };
   if constexpr (MAXO) {
     // the maximum over offsets takes two stages per pass over the offset blocks:
     // both are loaded (the second issued here, the first at the previous step),
@@ -768,19 +679,19 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     for (int kb = kw0; kb < kend; kb += 2 * STAGE) {
       if (kb + STAGE < kend) {
         load_stage<D, PAGED, MAXO>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
-        compute_max2(std::true_type{}, cA, cB, kb);
+        compute_max(std::true_type{}, cA, cB, kb);
       } else {
-        compute_max2(std::false_type{}, cA, cA, kb);
+        compute_max(std::false_type{}, cA, cA, kb);
       }
       if (kb + 2 * STAGE < kend) load_stage<D, PAGED, MAXO>(cA, a.k, u, g, kb + 2 * STAGE, kend, col, grp, s_bt, page0);
     }
   } else if (kw0 < kend) {
     for (int kb = kw0;; kb += 2 * STAGE) {
       load_stage<D, PAGED, MAXO>(cB, a.k, u, g, kb + STAGE, kend, col, grp, s_bt, page0);
-      compute_stage(cA, kb);
+      compute(cA, kb);
       if (kb + STAGE >= kend) break;
       load_stage<D, PAGED, MAXO>(cA, a.k, u, g, kb + 2 * STAGE, kend, col, grp, s_bt, page0);
-      compute_stage(cB, kb + STAGE);
+      compute(cB, kb + STAGE);
       if (kb + 2 * STAGE >= kend) break;
     }
   }
