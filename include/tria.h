@@ -178,7 +178,9 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max)
  *   agg         [device] fp32 [U][Hkv][n_max] aggregated scores; slots >= len[u]
  *               are left untouched
  *   ws          [device] workspace of ws_bytes >= tria_workspace_size(...)
- * Execution: the keys of each (unit, KV head) are scored in tiles of 2048 by
+ * Execution: the keys of each (unit, KV head) are scored in tiles of up to 2048
+ * (1024 for G > 4 or the maximum over offsets; balanced in multiples of 256 when
+ * n_max is larger, e.g. 1280 + 896 for 2176) by
  * concurrent workgroups that exchange their tile moments through the workspace
  * and wait (boundedly) for one another before normalising; this relies on the
  * hardware dispatching a kernel's workgroups in order, and reports
@@ -356,7 +358,8 @@ tria_status tria_stats_layer_budgets(int32_t n_units, const int32_t* unit_layer,
 /* Caps the number of workgroups tria_score's persistent kernel launches (0, the
  * default, means as many as the device holds at once), for callers that keep
  * compute units free for work on other streams.  A cap below the score tiles of
- * one (unit, KV head) (n_max / 2048, or n_max / 1024 when group > 4, rounded up)
+ * one (unit, KV head) (n_max / 2048, or n_max / 1024 when group > 4 or with the
+ * maximum over offsets, rounded up)
  * makes tria_score return TRIA_ESHAPE.  Results do not depend on the cap: every
  * tile's arithmetic and every reduction run in a fixed order.  Process-wide;
  * returns the previous cap. */

@@ -150,7 +150,7 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 // ------------------------------------------------------------------ workspace
 struct Layout {
   size_t B, Bmax, part, claim, hist, st, tiles, list, masks, total;
-  int32_t n_tiles, n_st;
+  int32_t tile, n_tiles, n_st;   // keys per score tile, score tiles and selection tiles per row
   tria::OffsetBlocks ob;
 };
 
@@ -162,8 +162,8 @@ size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   Layout L{};
   const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
-  const int tile = tria::score_tile_keys(p->group, p->offset_reduce == TRIA_OFFSETS_MAX);
-  L.n_tiles = (n_max + tile - 1) / tile;
+  L.tile = tria::score_tile_keys(p->group, p->offset_reduce == TRIA_OFFSETS_MAX, n_max);
+  L.n_tiles = (n_max + L.tile - 1) / L.tile;
   size_t off = 256;  // flag word
   L.B = off;
   off += al256(U * (size_t)p->n_kv_heads * (d / 16) * 64 * 16);  // MFMA B operands, 16 B per lane
@@ -221,12 +221,12 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
     return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if (n_units == 0 || n_max == 0) return TRIA_OK;
   const int omax = p->offset_reduce == TRIA_OFFSETS_MAX ? 1 : 0;
-  if (omax && tria::score_lds(p->head_dim, p->group, k->block_table != nullptr, 1, L.ob.nblk) > 160 * 1024)
+  if (omax && tria::score_lds(p->head_dim, p->group, k->block_table != nullptr, 1, L.ob.nblk, L.tile) > 160 * 1024)
     return fail(TRIA_ESHAPE, "maximum over %d offsets: %d coefficient blocks of head_dim %d do not fit in LDS",
                 p->n_offsets, L.ob.nblk, p->head_dim);
   // the tiles of one (unit, KV head) wait for each other: they must all fit at once
   const int cap = tria::score_capacity(p->head_dim, p->pairing, k->block_table != nullptr, p->group, omax,
-                                       L.ob.nblk);
+                                       L.ob.nblk, L.tile);
   if (cap < 0) return fail(TRIA_ELAUNCH, "k_score occupancy query failed");
   if (L.n_tiles > cap)
     return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the device holds %d",
@@ -250,14 +250,14 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
 
   tria::CoefArgs ca{n_units, p->n_kv_heads * p->group, p->n_kv_heads, p->head_dim, p->n_layers, p->pairing,
                     std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean,
-                    p->group, L.n_tiles, tria::score_tile_keys(p->group, omax), n_max, B,
+                    p->group, L.n_tiles, L.tile, n_max, B,
                     reinterpret_cast<uint64_t*>(part), next_tile, hist, flags, omax,
                     reinterpret_cast<uint32_t*>(w + L.Bmax), L.ob};
   hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
-                     tria::score_tile_keys(p->group, omax), L.n_tiles, p->agg,
+                     L.tile, L.n_tiles, p->agg,
                      len, B, raw, part, agg, next_tile, hist, flags, omax,
                      reinterpret_cast<const uint32_t*>(w + L.Bmax), L.ob};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, wg_cap, s); });

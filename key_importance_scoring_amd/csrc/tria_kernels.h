@@ -20,7 +20,18 @@ constexpr int kScoreTileMax = 2048;
 #define TRIA_SCORE_TILE_SMALL_G 2048
 #endif
 // (the maximum over offsets stages its coefficient blocks beside the tiles: 1024)
-inline int score_tile_keys(int group, int omax = 0) { return group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : 1024; }
+// Keys per score tile for rows of n_max slots: the fewest tiles the cap allows
+// (2048 keys for G <= 4 with the mean over offsets, else 1024: the tiles' scores
+// live in LDS), balanced in multiples of 256 (each wave takes a quarter of a tile
+// in 64-key stages), so that a row just past a multiple of the cap is not followed
+// by a nearly empty tile.
+inline int score_tile_keys(int group, int omax, int n_max) {
+  const int cap = group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : 1024;
+  if (n_max <= cap) return cap;
+  const int nt = (n_max + cap - 1) / cap;
+  const int t = ((n_max + nt - 1) / nt + 255) / 256 * 256;
+  return t < cap ? t : cap;
+}
 // A tile's published moments start as this bit pattern (cleared by k_coef): a NaN
 // whose low payload bits are set, which no moment computed from fp32 scores can
 // take (NaNs that arithmetic produces keep an fp32 payload or are the default one).
@@ -189,9 +200,9 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s);
 // Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
 // of one (unit, KV head) must be resident together for the moment exchange.
-int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk);
-// LDS bytes of one k_score workgroup
-size_t score_lds(int d, int group, bool paged, int omax, int nblk);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile);
+// LDS bytes of one k_score workgroup for tiles of `tile` keys
+size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile);
 // strategy: 0 automatic, 1 per group (when n_max fits), 2 tiled
 hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);

@@ -1850,8 +1850,7 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-size_t score_lds(int d, int group, bool paged, int omax, int nblk) {
-  const int tile = score_tile_keys(group, omax);
+size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile) {
   // two score buffers, a region that holds the tile's block ids during the score
   // phase and (the mean) the aggregate histogram during finalisation, the units'
   // lengths and tile prefix, and for the maximum over offsets the staged offset
@@ -1866,8 +1865,8 @@ size_t score_lds(int d, int group, bool paged, int omax, int nblk) {
   return ((base + 3) & ~(size_t)3) * 4 + (blocks > (size_t)kBins * 4 ? blocks : (size_t)kBins * 4);
 }
 
-int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk) {
-  const size_t lds = score_lds(d, group, paged, omax, nblk);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile) {
+  const size_t lds = score_lds(d, group, paged, omax, nblk, tile);
   int per_cu = 0, dev = 0, cus = 0;
   hipError_t e = hipErrorInvalidValue;
 #define TRIA_OCC_CASE(DD, PP, PG, MX)                                                                     \
@@ -1901,11 +1900,11 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
   const long tiles = (long)a.n_units * a.hkv * a.n_tiles;
   if (tiles == 0) return hipSuccess;
   const bool paged = a.k.bt != nullptr;
-  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk);
+  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk, a.tile);
   if (max_wg > 0 && max_wg < cap) cap = max_wg;
   if (cap < a.n_tiles) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
-  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk);
+  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk, a.tile);
 #define TRIA_SCORE_CASE(DD, PP, PG, MX)                                       \
   if (d == DD && pairing == PP && paged == PG && (a.omax != 0) == MX) {      \
     if (MX) hipLaunchKernelGGL((k_score_max<DD, PP, PG>), grid, blk, lds, s, a); \
