@@ -316,6 +316,19 @@ def test_full_size_sampled_units(name, keep_raw):
     _check_oracle_compaction(prob, kept)
 
 
+def test_row_at_resident_capacity():
+    """The longest row the score kernel takes: every tile of a (unit, KV head) must be
+    resident at once, 512 workgroups of 2048-key tiles on MI355X, so one row of
+    1,048,000 keys (512 tiles, the last one partial) against the oracle, with 100,000
+    kept and compacted."""
+    cfg = C["qwen3_8b"].replace(name="resident_max", n_layers=1, n_kv_heads=1, n_kv=1_048_000, budget=100_000)
+    log(f"[parity] {cfg.name}: one row of {cfg.n_kv} keys")
+    prob = _run(cfg)
+    assert prob.flags() == 0
+    kept = {0: check_unit(prob, 0)}
+    _check_oracle_compaction(prob, kept)
+
+
 # ----------------------------------------------------------------------------- schedule
 
 SCHED = {
