@@ -269,6 +269,49 @@ def test_device_flags_record_bad_metadata(strategy):
     assert int(prob.cnt[2].item()) == 3
 
 
+def test_statistics_follow_the_unit_layer_map():
+    """Each unit takes its statistics through its entry of the unit -> layer map, not
+    through its own index.  Relabelling the layers (moving the statistics' layer axis
+    and the map by the same permutation) leaves every output bit-identical; pointing
+    several units at one layer scores each of them with that layer's statistics."""
+    cfg = C["qwen3_8b"].replace(name="layer_map", n_layers=4, n_kv=3001, budget=700)
+    log(f"[parity] layer map: {cfg.n_units} units")
+    prob = DeviceProblem(cfg)
+    names = ("agg", "idx", "cnt", "K", "V", "pos")
+
+    def run():
+        for t in (prob.agg, prob.idx, prob.cnt, prob.pos_out):
+            t.fill_(-7)
+        prob.K_out.view(torch.int16).fill_(-7)
+        prob.V_out.view(torch.int16).fill_(-7)
+        prob.run()
+        torch.cuda.synchronize()
+        assert prob.flags() == 0
+        return [t.clone() for t in (prob.agg, prob.idx, prob.cnt, prob.K_out.view(torch.int16),
+                                    prob.V_out.view(torch.int16), prob.pos_out)]
+
+    ref = run()
+    perm = np.array([2, 0, 3, 1])                    # old layer l gets label perm[l]
+    pt = torch.from_numpy(perm).to(prob.dev)
+    for t in (prob.q_re, prob.q_im, prob.q_abs):
+        moved = torch.empty_like(t)
+        moved[pt] = t
+        t.copy_(moved)
+    prob.unit_layer.copy_(pt[prob.unit_layer.long()].to(torch.int32))
+    for r, g, what in zip(ref, run(), names):
+        assert torch.equal(r, g), f"relabelled layers: {what} differs"
+
+    # units 0, 1 and 3 on one layer, unit 2 on another (labels of the relabelled axis)
+    shared = np.array([1, 1, 3, 1], np.int32)
+    prob.unit_layer.copy_(torch.from_numpy(shared).to(prob.dev))
+    run()
+    re, im, ab = synth.q_stats(cfg)
+    src = np.argsort(perm)[shared]                   # the original layer each unit now reads
+    mu = (re.astype(np.float64) + 1j * im.astype(np.float64))[src]
+    for unit in range(cfg.n_units):
+        check_unit(prob, unit, mu=mu, absm=ab.astype(np.float64)[src])
+
+
 # ----------------------------------------------------------------------------- full sizes
 
 FULL_SAMPLES = {
