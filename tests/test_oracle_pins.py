@@ -283,6 +283,47 @@ def test_gqa_mapping_and_aggregation():
     np.testing.assert_allclose(o.aggregate_unit(raw, n, G, 2, 5, "max")[0][cand], zs.max(0)[cand])
 
 
+def test_gqa_two_heads_hand_values():
+    """Normalise each query head over the candidates first, then aggregate; the mean
+    carries the 1/G factor.  Hand values (tests/golden) for a group of two heads
+    whose raw scores have different means and spreads, so that the mean of the
+    per-head z-scores differs from their sum and from the z-score of the group's
+    mean raw score."""
+    t = _golden()["gqa_two_heads"]
+    inp = t["input"]
+    raw = np.array(inp["raw"])
+    G, sink, window = inp["group"], inp["sink"], inp["window"]
+    n = raw.shape[1]
+    for how in ("mean", "max"):
+        a = o.aggregate_unit(raw, n, G, sink, window, how)
+        assert a.shape == (1, n)
+        assert np.isinf(a[0, 0]) and np.isinf(a[0, -1]) and a[0, 0] > 0 and a[0, -1] > 0
+        np.testing.assert_allclose(a[0, 1:-1], t[how], rtol=0, atol=1e-14)
+    mean = o.aggregate_unit(raw, n, G, sink, window, "mean")[0, 1:-1]
+    assert np.abs(mean - np.array(t["not_sum"])).max() > 0.1
+    # the mean over a single head's z-scores is that head's z-score (G = 1)
+    np.testing.assert_allclose(o.aggregate_unit(raw[:1], n, 1, sink, window, "mean")[0, 1:-1],
+                               [-math.sqrt(1.5), 0.0, math.sqrt(1.5)], rtol=0, atol=1e-14)
+
+
+def test_gqa_mean_ranks_like_scaled_score_sum():
+    """A = (1/G) sum_h (s_h - m_h) / sigma_h = (1/G) sum_h s_h / sigma_h - c: the mean
+    aggregation ranks the slots as the sum of the raw scores, each divided by its
+    head's candidate standard deviation (computed here with numpy's std), does."""
+    rng = np.random.default_rng(23)
+    G, n, sink, window = 4, 200, 3, 17
+    scale = np.array([0.5, 3.0, 40.0, 1e3])[:, None]
+    shift = np.array([-7.0, 0.0, 250.0, 1e4])[:, None]
+    raw = rng.normal(size=(G, n)) * scale + shift
+    cand = ~o.protected_mask(n, sink, window)
+    sd = raw[:, cand].std(axis=1)
+    direct = (raw / sd[:, None]).sum(axis=0)[cand]
+    a = o.aggregate_unit(raw, n, G, sink, window, "mean")[0][cand]
+    c = float(np.sum(raw[:, cand].mean(axis=1) / sd))
+    np.testing.assert_allclose(a, (direct - c) / G, rtol=0, atol=1e-10)
+    np.testing.assert_array_equal(np.argsort(-a, kind="stable"), np.argsort(-direct, kind="stable"))
+
+
 def test_scaling_stats_leaves_selection_unchanged():
     rng = np.random.default_rng(19)
     cfg = synth.CONFIGS["tiny"].replace(n_kv=300, budget=120, window=40, sink=2)
