@@ -238,11 +238,14 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
  *   K row (u, g, j) <- K row (u, g, idx[u][g][j]);  V likewise;
  *   pos[u][g][j] <- pos[u][g][idx[u][g][j]]   (when pos is not NULL)
  * with idx as tria_select writes it: ascending, so idx[j] >= j.  Rows with
- * idx[j] == j are not touched; slots >= cnt[u] keep whatever they held.
+ * idx[j] == j are not touched; slots >= cnt[u] keep whatever they held.  Then
+ * len[u] <- the unit's kept count, min(cnt[u], b_max, len[u]) (negative values
+ * count as 0), so that the next append lands right after the kept rows.
  *   k, v        [device] cache views (dense or paged; the same layouts as
  *               tria_compact's sources), read and written
  *   pos         [device] int32 [U][Hkv][n_max] per-head positions, or NULL
- *   len, idx, cnt, b_max, n_max as for tria_compact
+ *   len         [device] int32 [U], read, then overwritten with the kept count
+ *   idx, cnt, b_max, n_max as for tria_compact
  * Each (unit, KV head) is moved by one workgroup in ascending chunks of 128 rows,
  * a chunk's reads completing before its writes: with ascending indices no row is
  * overwritten before it is read.  An index that is not ascending, below its row
@@ -251,12 +254,17 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
  * views must not overlap each other.
  */
 tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
-                                 int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+                                 int32_t n_units, int32_t n_max, int32_t b_max, int32_t* len,
                                  const int32_t* idx, const int32_t* cnt, void* ws, void* stream);
 
 /* tria_append - writes t_new new rows per (unit, KV head) at slots len[u] ..
- * len[u] + t_new - 1 (the decode loop's generated tokens; the caller advances len
- * afterwards).
+ * len[u] + t_new - 1 (the decode loop's generated tokens), then advances the
+ * unit's state on the device: len[u] <- min(len[u] + t_new, n_max) and, when
+ * q_pos and pos_new are given, q_pos[u] <- pos_new[u][t_new - 1] (the newest
+ * token is the current query of the next tria_score) [Calib issue: the port
+ * tracks n_kv between prunes every 128 tokens].
+ *   len         [device] int32 [U], read, then advanced
+ *   q_pos       [device] int32 [U], or NULL (then not written)
  *   k_new, v_new [device] bf16 [U][Hkv][t_new][d], rows already rotated at their
  *               positions (as a model caches them)
  *   pos_new     [device] int32 [U][t_new] their positions, written to every
@@ -264,8 +272,8 @@ tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, co
  * Slots at or past n_max are flagged (TRIA_FLAG_LEN) and skipped.
  */
 tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
-                        int32_t n_units, int32_t n_max, const int32_t* len, int32_t t_new, const void* k_new,
-                        const void* v_new, const int32_t* pos_new, void* ws, void* stream);
+                        int32_t n_units, int32_t n_max, int32_t* len, int32_t* q_pos, int32_t t_new,
+                        const void* k_new, const void* v_new, const int32_t* pos_new, void* ws, void* stream);
 
 /* tria_calibrate - the calibrated query statistics tria_score reads, from a stream
  * of pre-RoPE query rows [Calib issue, "How it works": per (layer, head, band)

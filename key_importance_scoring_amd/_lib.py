@@ -112,7 +112,8 @@ def load() -> ctypes.CDLL:
                                          c_void_p]
     lib.tria_append.restype = c_int32
     lib.tria_append.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_void_p, c_int32,
-                                c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+                                c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p]
     lib.tria_stats_parse.restype = c_int32
     lib.tria_stats_parse.argtypes = [c_void_p, c_size_t, POINTER(TriaStatsInfo), c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p]
@@ -213,10 +214,11 @@ def tria_compact_inplace(p: TriaParams, k: TriaKvView, v: TriaKvView, pos, n_uni
                                        b_max, ptr(len_), ptr(idx), ptr(cnt), ptr(ws), stream_handle(stream)))
 
 
-def tria_append(p: TriaParams, k: TriaKvView, v: TriaKvView, pos, n_units: int, n_max: int, len_, t_new: int,
-                k_new, v_new, pos_new, ws, stream=None) -> None:
+def tria_append(p: TriaParams, k: TriaKvView, v: TriaKvView, pos, n_units: int, n_max: int, len_, q_pos,
+                t_new: int, k_new, v_new, pos_new, ws, stream=None) -> None:
     _check(load().tria_append(ctypes.byref(p), ctypes.byref(k), ctypes.byref(v), ptr(pos), n_units, n_max, ptr(len_),
-                              t_new, ptr(k_new), ptr(v_new), ptr(pos_new), ptr(ws), stream_handle(stream)))
+                              ptr(q_pos), t_new, ptr(k_new), ptr(v_new), ptr(pos_new), ptr(ws),
+                              stream_handle(stream)))
 
 
 def tria_device_flags(ws, stream=None) -> int:

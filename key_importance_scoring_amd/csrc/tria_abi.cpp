@@ -385,7 +385,7 @@ tria_status tria_calibrate(const tria_params* p, const void* q, int64_t stride_l
 }
 
 tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
-                                 int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+                                 int32_t n_units, int32_t n_max, int32_t b_max, int32_t* len,
                                  const int32_t* idx, const int32_t* cnt, void* ws, void* stream) {
   tria_status st = check_params(p);
   if (st != TRIA_OK) return st;
@@ -409,8 +409,8 @@ tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, co
 }
 
 tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t* pos,
-                        int32_t n_units, int32_t n_max, const int32_t* len, int32_t t_new, const void* k_new,
-                        const void* v_new, const int32_t* pos_new, void* ws, void* stream) {
+                        int32_t n_units, int32_t n_max, int32_t* len, int32_t* q_pos, int32_t t_new,
+                        const void* k_new, const void* v_new, const int32_t* pos_new, void* ws, void* stream) {
   tria_status st = check_params(p);
   if (st != TRIA_OK) return st;
   if (n_units < 0 || n_max < 0 || t_new < 0) return fail(TRIA_EINVAL, "n_units, n_max and t_new must be >= 0");
@@ -421,7 +421,7 @@ tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_
     return fail(TRIA_ESHAPE, "k_new and v_new must be 16-byte aligned");
   if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL (its flag word records contract violations)");
   if (n_units == 0 || t_new == 0) return TRIA_OK;
-  tria::AppendArgs aa{mkview(k), mkview(v), pos, n_units, n_max, p->n_kv_heads, p->head_dim, t_new, len,
+  tria::AppendArgs aa{mkview(k), mkview(v), pos, n_units, n_max, p->n_kv_heads, p->head_dim, t_new, len, q_pos,
                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), pos_new,
                       static_cast<int32_t*>(ws)};
   hipStream_t s = static_cast<hipStream_t>(stream);

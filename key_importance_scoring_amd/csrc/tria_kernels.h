@@ -215,7 +215,7 @@ struct InplaceArgs {
   MutKView k, v;
   int32_t* pos;               // [U][Hkv][n_max] per-head positions, or null
   int32_t n_units, n_max, b_max, hkv, d;
-  const int32_t* len;
+  int32_t* len;               // read by the move, then set to the kept count
   const int32_t* idx;         // [U][Hkv][b_max]
   const int32_t* cnt;
   int32_t* flags;
@@ -227,7 +227,8 @@ struct AppendArgs {
   MutKView k, v;
   int32_t* pos;               // [U][Hkv][n_max] or null
   int32_t n_units, n_max, hkv, d, t_new;
-  const int32_t* len;
+  int32_t* len;               // read by the append, then advanced by t_new
+  int32_t* q_pos;             // [U] or null: set to the newest appended position
   const uint16_t* k_new;      // [U][Hkv][t_new][d]
   const uint16_t* v_new;      // [U][Hkv][t_new][d]
   const int32_t* pos_new;     // [U][t_new] or null

@@ -396,11 +396,15 @@ template <int D, bool MAXO = false>
 constexpr int stage_blocks() {
   return MAXO ? (D >= 256 ? 2 : 4) : (D >= 256 ? (TRIA_SCORE_NBI + 1) / 2 : TRIA_SCORE_NBI);
 }
-// a wave's keys (tile / 4, tiles of 1024 or 2048) must be whole stages: a stage's
-// scores are written to LDS for all its keys, and a partial last stage would write
-// into the next wave's range
-static_assert((1024 / 4) % (16 * stage_blocks<64>()) == 0 && (1024 / 4) % (16 * stage_blocks<256>()) == 0,
-              "stage size must divide a wave's keys");
+// a wave's keys must be whole stages: a stage's scores are written to LDS for all its
+// keys, and a partial last stage would write into the next wave's range.  Tiles are
+// multiples of 256 keys (score_tile_keys balances them in steps of 256), so a wave
+// takes a multiple of 64 keys: every stage size must divide 64.
+template <int D, bool MAXO>
+constexpr bool stage_divides_64() { return 64 % (16 * stage_blocks<D, MAXO>()) == 0; }
+static_assert(stage_divides_64<64, false>() && stage_divides_64<128, false>() && stage_divides_64<256, false>() &&
+                  stage_divides_64<64, true>() && stage_divides_64<128, true>() && stage_divides_64<256, true>(),
+              "stage size must divide a wave's share of a tile (a multiple of 64 keys)");
 
 // One pipeline stage of a wave: stage_blocks blocks of 16 keys, d/32 16-byte chunks per lane each.
 template <int D, bool MAXO = false>
@@ -1803,6 +1807,16 @@ __global__ __launch_bounds__(256) void k_compact_inplace(InplaceArgs a) {
   }
 }
 
+// After the move: the unit now holds its kept count, len[u] <- cnt[u] (clamped as the
+// move clamped it).  A kernel of its own, so that every (unit, KV head) of the move
+// has read len[u] before it changes.
+__global__ __launch_bounds__(256) void k_set_len(InplaceArgs a) {
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= a.n_units) return;
+  const int n = min(max(a.len[u], 0), a.n_max);
+  a.len[u] = min(max(a.cnt[u], 0), min(a.b_max, n));
+}
+
 // Appends t_new rows of each (unit, KV head) at slots len[u] + t (K, V and the
 // unit's positions into every head's position row); slots past n_max are flagged.
 __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
@@ -1823,6 +1837,17 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a) {
     if (vd) reinterpret_cast<u32x4*>(vd)[part] = reinterpret_cast<const u32x4*>(a.v_new + src)[part];
     if (a.pos && a.pos_new && part == 0) a.pos[(size_t)ug * a.n_max + sl] = a.pos_new[(size_t)u * a.t_new + t];
   }
+}
+
+// After the rows are in: len[u] <- min(len[u] + t_new, n_max) and, with positions
+// given, the current query position q_pos[u] <- the newest appended position.  A
+// kernel of its own, so that every block of k_append has read len[u] first.
+__global__ __launch_bounds__(256) void k_append_advance(AppendArgs a) {
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= a.n_units) return;
+  const int n0 = max(a.len[u], 0);
+  a.len[u] = min(n0 + a.t_new, a.n_max);
+  if (a.q_pos && a.pos_new) a.q_pos[u] = a.pos_new[(size_t)u * a.t_new + a.t_new - 1];
 }
 
 // ============================================================================ launches
@@ -2016,6 +2041,9 @@ hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s) {
   else if (a.d == 128) hipLaunchKernelGGL(k_compact_inplace<128>, grid, dim3(256), 0, s, a);
   else if (a.d == 256) hipLaunchKernelGGL(k_compact_inplace<256>, grid, dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_set_len, dim3((unsigned)((a.n_units + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -2024,6 +2052,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   const int rpp = 256 / (a.d / 8);
   const unsigned gy = (unsigned)min((a.t_new + rpp - 1) / rpp, 64);
   hipLaunchKernelGGL(k_append, dim3((unsigned)(a.n_units * a.hkv), gy), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_append_advance, dim3((unsigned)((a.n_units + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

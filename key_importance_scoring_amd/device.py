@@ -24,6 +24,41 @@ def _bf16(arr: np.ndarray, device) -> torch.Tensor:
     return t.to(device).view(torch.bfloat16)
 
 
+# Guard regions around every output buffer: GUARD elements before and after, filled
+# with a canary the kernels never write, so that a write outside a buffer's extent
+# shows up as a changed canary (check_guards).
+GUARD = 2048
+# canaries by element size, written through an integer view (for fp32: a NaN whose
+# payload no kernel produces)
+_CANARY = {1: 0xA5, 2: -0x5A5B, 4: 0x7FA5A5A5}
+_INT_VIEW = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+
+
+class Guarded:
+    """Output tensors allocated inside larger buffers with canary-filled guards."""
+
+    def __init__(self, device):
+        self.device = device
+        self.bufs = []
+
+    def zeros(self, shape, dtype):
+        n = 1
+        for x in shape:
+            n *= int(x)
+        buf = torch.empty(n + 2 * GUARD, dtype=dtype, device=self.device)
+        bits = buf.view(_INT_VIEW[buf.element_size()])
+        bits.fill_(_CANARY[buf.element_size()])
+        bits[GUARD:GUARD + n].zero_()
+        self.bufs.append((bits, n))
+        return buf[GUARD:GUARD + n].view(*shape)
+
+    def check(self) -> None:
+        for bits, n in self.bufs:
+            c = _CANARY[bits.element_size()]
+            if not (bool((bits[:GUARD] == c).all()) and bool((bits[GUARD + n:] == c).all())):
+                raise AssertionError(f"a guard region of a {n}-element {bits.dtype} buffer was overwritten")
+
+
 def params_for(cfg: synth.Config) -> L.TriaParams:
     return L.make_params(cfg.head_dim, cfg.n_kv_heads, cfg.group, cfg.n_layers,
                          L.PAIR_NEOX if cfg.pairing == "neox" else L.PAIR_INTERLEAVED,
@@ -69,6 +104,8 @@ class DeviceProblem:
         self.V = _bf16(v_host, self.dev)
         del v_host
 
+        self.guards = Guarded(self.dev)
+        gz = self.guards.zeros
         if cfg.paged:
             pg = synth.paging(cfg)
             self.paging = pg
@@ -77,8 +114,8 @@ class DeviceProblem:
             bs = cfg.block_size
             self.k_view = L.make_view(self.K, 0, d, Hkv * d, self.bt, bs, pg.block_table.shape[1], pg.n_blocks)
             self.v_view = L.make_view(self.V, 0, d, Hkv * d, self.bt, bs, pg.block_table.shape[1], pg.n_blocks)
-            self.K_out = torch.zeros((pg.n_dst_blocks, bs, Hkv, d), dtype=torch.bfloat16, device=self.dev)
-            self.V_out = torch.zeros_like(self.K_out)
+            self.K_out = gz((pg.n_dst_blocks, bs, Hkv, d), torch.bfloat16)
+            self.V_out = gz((pg.n_dst_blocks, bs, Hkv, d), torch.bfloat16)
             mdb = pg.dst_block_table.shape[1]
             self.kd_view = L.make_view(self.K_out, 0, d, Hkv * d, self.dbt, bs, mdb, pg.n_dst_blocks)
             self.vd_view = L.make_view(self.V_out, 0, d, Hkv * d, self.dbt, bs, mdb, pg.n_dst_blocks)
@@ -87,8 +124,8 @@ class DeviceProblem:
             nm = self.K.shape[2]
             self.k_view = L.make_view(self.K, Hkv * nm * d, nm * d, d)
             self.v_view = L.make_view(self.V, Hkv * nm * d, nm * d, d)
-            self.K_out = torch.zeros((U, Hkv, self.b_max, d), dtype=torch.bfloat16, device=self.dev)
-            self.V_out = torch.zeros_like(self.K_out)
+            self.K_out = gz((U, Hkv, self.b_max, d), torch.bfloat16)
+            self.V_out = gz((U, Hkv, self.b_max, d), torch.bfloat16)
             self.kd_view = L.make_view(self.K_out, Hkv * self.b_max * d, self.b_max * d, d)
             self.vd_view = L.make_view(self.V_out, Hkv * self.b_max * d, self.b_max * d, d)
 
@@ -107,13 +144,13 @@ class DeviceProblem:
 
         # --- outputs and workspace
         Hq = cfg.n_q_heads
-        self.raw = torch.zeros((U, Hq, self.n_max), dtype=torch.float32, device=self.dev) if keep_raw else None
-        self.agg = torch.zeros((U, Hkv, self.n_max), dtype=torch.float32, device=self.dev)
-        self.idx = torch.zeros((U, Hkv, self.b_max), dtype=torch.int32, device=self.dev)
-        self.cnt = torch.zeros((U,), dtype=torch.int32, device=self.dev)
-        self.pos_out = torch.zeros((U, Hkv, self.b_max), dtype=torch.int32, device=self.dev)
+        self.raw = gz((U, Hq, self.n_max), torch.float32) if keep_raw else None
+        self.agg = gz((U, Hkv, self.n_max), torch.float32)
+        self.idx = gz((U, Hkv, self.b_max), torch.int32)
+        self.cnt = gz((U,), torch.int32)
+        self.pos_out = gz((U, Hkv, self.b_max), torch.int32)
         self.ws_bytes = L.tria_workspace_size(self.params, U, self.n_max)
-        self.ws = torch.zeros((self.ws_bytes,), dtype=torch.uint8, device=self.dev)
+        self.ws = gz((self.ws_bytes,), torch.uint8)
 
     def _host_cache(self, which: str, workers) -> np.ndarray:
         return host_cache(self.cfg, which, workers)
@@ -139,6 +176,10 @@ class DeviceProblem:
 
     def flags(self) -> int:
         return L.tria_device_flags(self.ws, torch.cuda.current_stream(self.dev))
+
+    def check_guards(self) -> None:
+        """Raises if a kernel wrote outside any output buffer (or the workspace)."""
+        self.guards.check()
 
     # ------------------------------------------------------------------ readback helpers
     def kept(self, unit: int, kv_head: int) -> np.ndarray:

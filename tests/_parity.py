@@ -106,6 +106,63 @@ def check_compaction(prob, unit: int, g: int, kept: np.ndarray, what: str) -> No
                                   err_msg=f"{what} pos")
 
 
+def _pool_init():
+    """Worker set-up: one BLAS thread per process (the pool already spans the cores)."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def _oracle_pair(args):
+    cfg, unit, g, form, want_raw = args
+    raw, agg, kept = oracle_head(cfg, unit, g, form)
+    return (raw if want_raw else None), agg, kept
+
+
+def oracle_pairs(cfg, pairs, form: str = "folded", want_raw: bool = False, workers: int | None = None):
+    """oracle_head for every (unit, KV head) in `pairs`, in a process pool over the
+    host cores (spawned processes; at most 16).  Yields (pair, raw or None, agg,
+    kept) in the order of `pairs`."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import os
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    jobs = [(cfg, unit, g, form, want_raw) for unit, g in pairs]
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                                initializer=_pool_init) as ex:
+        for pair, res in zip(pairs, ex.map(_oracle_pair, jobs, chunksize=2)):
+            yield (pair, *res)
+
+
+def check_compaction_on_device(prob, what: str) -> None:
+    """Every (unit, KV head): the compacted K and V rows and positions equal the
+    source's rows at the kept slots, gathered by torch on the device (an independent
+    gather), for j < cnt[u]."""
+    import torch
+    cfg = prob.cfg
+    d, bs = cfg.head_dim, cfg.block_size
+    cnt = prob.cnt.cpu().numpy()
+    for unit in range(cfg.n_units):
+        k = int(cnt[unit])
+        if k == 0:
+            continue
+        ix = prob.idx[unit, :, :k].long()                              # [Hkv][k]
+        heads = torch.arange(cfg.n_kv_heads, device=ix.device)[:, None]
+        j = torch.arange(k, device=ix.device)[None, :]
+        for which in ("k", "v"):
+            src = prob.K if which == "k" else prob.V
+            dst = prob.K_out if which == "k" else prob.V_out
+            if cfg.paged:
+                bt, dbt = prob.bt[unit].long(), prob.dbt[unit].long()
+                want = src[bt[ix // bs], ix % bs, heads]
+                got = dst[dbt[j // bs], j % bs, heads]
+            else:
+                want = src[unit, heads, ix]
+                got = dst[unit, :, :k]
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{what} unit {unit}: {which} rows"
+        want_pos = prob.pos[unit, 0][ix]
+        assert torch.equal(prob.pos_out[unit, :, :k], want_pos), f"{what} unit {unit}: positions"
+
+
 def check_unit(prob, unit: int, heads=None, form: str = "folded", mu=None, absm=None):
     """Full comparison of one unit (optionally a subset of its KV heads).  Returns the
     oracle kept sets {kv_head: slots}."""

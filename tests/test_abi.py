@@ -286,7 +286,7 @@ def test_append_checks():
     p = _params()
     k = _view(A)
     v = _view(A + 2 * 8 * 4096 * 128 * 2)
-    call = lambda **kw: L.tria_append(p, k, v, None, 2, 4096, A, kw.get("t", 128), kw.get("kn", A), A, None,
+    call = lambda **kw: L.tria_append(p, k, v, None, 2, 4096, A, None, kw.get("t", 128), kw.get("kn", A), A, None,
                                       kw.get("ws", WS))
     assert _status(lambda: call(kn=None)) == L.TRIA_EINVAL
     assert _status(lambda: call(kn=A + 8)) == L.TRIA_ESHAPE

@@ -64,6 +64,11 @@ def _drive(loop, cfg, budget, interval, steps, pairs, name):
         pruned = loop.step(rows=(kn, vn, pn))
         torch.cuda.synchronize()
         assert loop.flags() == 0
+        loop.check_guards()
+        # the library advanced the device state: lengths (append, then the kept
+        # count after a prune) and the newest position as the query position
+        np.testing.assert_array_equal(loop.len.cpu().numpy(), loop.len_host)
+        np.testing.assert_array_equal(loop.q_pos.cpu().numpy(), loop.next_pos - 1)
         if not pruned:
             continue
         checked += 1
@@ -164,9 +169,11 @@ def test_inplace_matches_out_of_place():
     vdv = L.make_view(Vd, Hkv * b_max * d, b_max * d, d)
     P = t(pos)
     L.tria_compact(p, kv, vv, P, Hkv, U, n_max, b_max, t(lens), t(idx), t(cnt), kdv, vdv, Pd)
-    L.tria_compact_inplace(p, kv, vv, P, U, n_max, b_max, t(lens), t(idx), t(cnt), ws)
+    lens_d = t(lens)
+    L.tria_compact_inplace(p, kv, vv, P, U, n_max, b_max, lens_d, t(idx), t(cnt), ws)
     torch.cuda.synchronize()
     assert L.tria_device_flags(ws) == 0
+    np.testing.assert_array_equal(lens_d.cpu().numpy(), cnt)          # len <- the kept count
     Kh, Vh, Ph = K.cpu().numpy(), V.cpu().numpy(), P.cpu().numpy()
     Kdh, Vdh, Pdh = Kd.cpu().numpy(), Vd.cpu().numpy(), Pd.cpu().numpy()
     for u in range(U):
@@ -195,10 +202,46 @@ def test_inplace_flags_descending_indices():
     vv = L.make_view(V, n_max * d, n_max * d, d)
     idx = torch.tensor([[[0, 1, 9, 5, 20, 21, 22, 23]]], dtype=torch.int32, device=dev)
     ws = torch.zeros(256, dtype=torch.uint8, device=dev)
-    L.tria_compact_inplace(p, kv, vv, None, 1, n_max, b_max, torch.tensor([40], dtype=torch.int32, device=dev), idx,
+    lens_d = torch.tensor([40], dtype=torch.int32, device=dev)
+    L.tria_compact_inplace(p, kv, vv, None, 1, n_max, b_max, lens_d, idx,
                            torch.tensor([8], dtype=torch.int32, device=dev), ws)
     torch.cuda.synchronize()
+    assert int(lens_d[0]) == 8
     assert L.tria_device_flags(ws) & L.FLAG_INDEX
     # rows 0, 1 stay; row 2 <- row 9; row 3 (index 5 < 9) is left; rows 4.. <- 20..
     assert torch.equal(K[0, 0, 2], k0[0, 0, 9]) and torch.equal(K[0, 0, 3], k0[0, 0, 3])
     assert torch.equal(K[0, 0, 4], k0[0, 0, 20]) and torch.equal(V[0, 0, 7], v0[0, 0, 23])
+
+
+def test_append_advances_len_and_query_position():
+    """tria_append writes the rows at len[u] .., then len[u] <- min(len[u] + t, n_max)
+    and q_pos[u] <- the newest position; rows that would land past n_max are skipped
+    and flagged."""
+    d, Hkv, U, n_max, t_new = 64, 2, 3, 64, 8
+    dev = "cuda:0"
+    p = L.make_params(d, Hkv, 1, 1, L.PAIR_NEOX, L.AGG_MAX, 1e6, [1], 0, 0)
+    K = torch.zeros((U, Hkv, n_max, d), dtype=torch.int16, device=dev)
+    V = torch.zeros_like(K)
+    P = torch.full((U, Hkv, n_max), -1, dtype=torch.int32, device=dev)
+    kv = L.make_view(K, Hkv * n_max * d, n_max * d, d)
+    vv = L.make_view(V, Hkv * n_max * d, n_max * d, d)
+    rng = np.random.default_rng(11)
+    kn = torch.from_numpy(rng.integers(-30000, 30000, size=(U, Hkv, t_new, d), dtype=np.int16)).to(dev)
+    vn = torch.from_numpy(rng.integers(-30000, 30000, size=(U, Hkv, t_new, d), dtype=np.int16)).to(dev)
+    pn = torch.from_numpy((np.arange(U * t_new, dtype=np.int32) * 3 + 100).reshape(U, t_new)).to(dev)
+    lens0 = np.array([0, 10, n_max - 5], np.int32)
+    lens = torch.from_numpy(lens0.copy()).to(dev)
+    q_pos = torch.zeros(U, dtype=torch.int32, device=dev)
+    ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+    L.tria_append(p, kv, vv, P, U, n_max, lens, q_pos, t_new, kn, vn, pn, ws)
+    torch.cuda.synchronize()
+    assert L.tria_device_flags(ws) == L.FLAG_LEN                     # unit 2 runs past n_max
+    np.testing.assert_array_equal(lens.cpu().numpy(), np.minimum(lens0 + t_new, n_max))
+    np.testing.assert_array_equal(q_pos.cpu().numpy(), pn[:, -1].cpu().numpy())
+    for u in range(U):
+        fit = min(t_new, n_max - int(lens0[u]))
+        sl = slice(int(lens0[u]), int(lens0[u]) + fit)
+        assert torch.equal(K[u, :, sl], kn[u, :, :fit]) and torch.equal(V[u, :, sl], vn[u, :, :fit])
+        for g in range(Hkv):
+            assert torch.equal(P[u, g, sl], pn[u, :fit])
+    assert (K[0, :, t_new:] == 0).all()                               # nothing past the new rows

@@ -4,14 +4,15 @@ Small cases run every unit and KV head element by element; they span several
 score tiles (2048 keys) with ragged tails, both pairings, head dims 64/128/256,
 mean and max aggregation, paged caches and the degenerate budgets.  The full-size
 workloads run in the same launch configuration as the benchmark and are checked
-on sampled units (every key of each sampled (unit, KV head), since the z-norm and
-the top-B depend on all of them).
+on every (unit, KV head) against the folded oracle (in a process pool over the
+host cores), and on sampled pairs against the literal loop over the offsets.
 """
 import numpy as np
 import pytest
 import torch
 
-from _parity import check_compaction, check_kept, check_raw, check_unit, log, oracle_head
+from _parity import (check_agg, check_compaction, check_compaction_on_device, check_kept, check_raw,
+                     check_unit, log, oracle_head, oracle_pairs)
 from oracle import tria_oracle as o
 from key_importance_scoring_amd import _lib as L
 from key_importance_scoring_amd import synth
@@ -57,6 +58,7 @@ def _run(cfg, **kw):
     prob = DeviceProblem(cfg, **kw)
     prob.run()
     torch.cuda.synchronize()
+    prob.check_guards()
     return prob
 
 
@@ -72,6 +74,7 @@ def _oracle_idx(prob, kept_by_unit):
 def _check_oracle_compaction(prob, kept_by_unit):
     prob.compact(idx=_oracle_idx(prob, kept_by_unit))
     torch.cuda.synchronize()
+    prob.check_guards()
     for unit, per_head in kept_by_unit.items():
         for g, kept in per_head.items():
             check_compaction(prob, unit, g, kept, f"{prob.cfg.name} unit {unit} kv {g} (oracle idx)")
@@ -314,48 +317,73 @@ def test_statistics_follow_the_unit_layer_map():
 
 # ----------------------------------------------------------------------------- full sizes
 
+# pairs that are also checked with the literal offset loop (the direct form) and
+# compacted on the host from regenerated rows
 FULL_SAMPLES = {
-    "qwen3_8b": [(0, None), (35, None)],
-    "qwen3_32b": [(0, None), (63, None)],
-    "batched_decode": [(0, None), (37, None), (63, None)],
-    "long_context": [(0, [0, 5, 7])],
+    "qwen3_8b": [(0, 0), (17, 3), (35, 7)],
+    "qwen3_32b": [(0, 0), (63, 7)],
+    "batched_decode": [(0, 0), (37, 5), (63, 7)],
+    "long_context": [(0, 5)],
 }
 
 
-def _nonconc_unit(cfg):
+def _nonconc_pair(cfg):
     nc = synth.nonconcentrated(cfg)
-    rows = np.nonzero(nc.any(axis=1))[0]
-    return int(rows[0]) if rows.size else 0
+    rows = np.argwhere(nc)
+    return (int(rows[0][0]), int(rows[0][1])) if rows.size else (0, 0)
 
 
 @pytest.mark.parametrize("name,keep_raw", [(n, False) for n in FULL_SAMPLES] + [("qwen3_8b", True)])
-def test_full_size_sampled_units(name, keep_raw):
-    """keep_raw=False is the benchmark's launch configuration (no per-query-head
-    scores written); keep_raw=True also checks those scores at full size."""
+def test_full_size_every_unit(name, keep_raw):
+    """Every (unit, KV head) of the full-size workloads against the folded fp64 oracle
+    (aggregates element by element, kept sets, and with keep_raw the per-query-head
+    scores), in the benchmark's launch configuration when keep_raw is False; the
+    oracle runs in a process pool over the host cores.  Compaction: every pair
+    against a device gather of its source rows, sampled pairs on the host from
+    regenerated rows and with the oracle's kept slots.  Sampled pairs are also
+    scored with the literal loop over the offsets."""
     cfg = C[name]
     prob = _run(cfg, keep_raw=keep_raw)
     assert prob.flags() == 0
-    samples = list(FULL_SAMPLES[name])
-    if name == "qwen3_32b":
-        samples.append((_nonconc_unit(cfg), None))
-    kept = {}
-    for unit, heads in samples:
-        log(f"[parity] {name}: checking unit {unit}")
-        kept[unit] = check_unit(prob, unit, heads=heads)
-    # properties that hold for every unit: counts, ranges, protected slots kept
     u = synth.units(cfg)
     cnt = prob.cnt.cpu().numpy()
     np.testing.assert_array_equal(cnt, np.minimum(u.budget, u.lengths))
+    agg = prob.agg.cpu().numpy()
     idx = prob.idx.cpu().numpy()
-    for unit in range(cfg.n_units):
-        n = int(u.lengths[unit])
-        k = int(cnt[unit])
-        blk = idx[unit, :, :k]
-        assert (np.diff(blk, axis=1) > 0).all() and (blk >= 0).all() and (blk < n).all()
-        prot = np.nonzero(o.protected_mask(n, cfg.sink, cfg.window))[0]
-        for g in range(cfg.n_kv_heads):
-            assert np.isin(prot, blk[g]).all()
-        assert (idx[unit, :, k:] == -1).all()
+    raw = prob.raw.cpu().numpy() if keep_raw else None
+    G = cfg.group
+    pairs = [(unit, g) for unit in range(cfg.n_units) for g in range(cfg.n_kv_heads)]
+    log(f"[parity] {name}: oracle over {len(pairs)} (unit, KV head) pairs")
+    done = 0
+    for (unit, g), o_raw, o_agg, o_kept in oracle_pairs(cfg, pairs, want_raw=keep_raw):
+        n, k = int(u.lengths[unit]), int(cnt[unit])
+        what = f"{name} unit {unit} kv {g}"
+        if keep_raw:
+            check_raw(raw[unit, g * G:(g + 1) * G, :n], o_raw, what)
+        check_agg(agg[unit, g, :n], o_agg, what)
+        check_kept(idx[unit, g, :k].astype(np.int64), o_kept, o_agg, n, int(u.budget[unit]), cfg.sink,
+                   cfg.window, what)
+        assert (idx[unit, g, k:] == -1).all(), what
+        done += 1
+        if done % 64 == 0:
+            log(f"[parity] {name}: {done} pairs checked")
+    assert done == len(pairs)
+    check_compaction_on_device(prob, name)
+    samples = list(FULL_SAMPLES[name])
+    if name == "qwen3_32b":
+        samples.append(_nonconc_pair(cfg))
+    log(f"[parity] {name}: {len(samples)} pairs with the direct form")
+    kept = {}
+    for (unit, g), o_raw, o_agg, o_kept in oracle_pairs(cfg, samples, form="direct", want_raw=keep_raw):
+        n, k = int(u.lengths[unit]), int(cnt[unit])
+        what = f"{name} unit {unit} kv {g} (direct form)"
+        if keep_raw:
+            check_raw(raw[unit, g * G:(g + 1) * G, :n], o_raw, what)
+        check_agg(agg[unit, g, :n], o_agg, what)
+        g_kept = idx[unit, g, :k].astype(np.int64)
+        check_kept(g_kept, o_kept, o_agg, n, int(u.budget[unit]), cfg.sink, cfg.window, what)
+        check_compaction(prob, unit, g, g_kept, what)
+        kept.setdefault(unit, {})[g] = o_kept
     _check_oracle_compaction(prob, kept)
 
 
