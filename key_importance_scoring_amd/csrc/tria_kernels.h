@@ -83,7 +83,13 @@ struct Offsets {
   int32_t n;
 };
 
+// Sample slots per (unit, KV head) whose mean band magnitudes are the norm term's
+// reference magnitudes (spread evenly over the unit's keys).
+constexpr int kRefRows = 16;
+static_assert(kRefRows % 8 == 0, "k_coef spreads the sample rows evenly over the 256 / F (at most 8) threads of a band");
+
 struct CoefArgs {
+  KView k;                    // the K cache: sample rows for the reference magnitudes
   int32_t n_units, hq, hkv, d, layers, pairing;
   double log_base;            // ln(theta)
   const int32_t* len;
@@ -94,7 +100,8 @@ struct CoefArgs {
   const float* q_abs;
   int32_t group, n_tiles, tile;  // query heads per KV head; score tiles per (unit, KV head), keys per tile
   int32_t n_max;
-  uint32_t* B;                // [U][Hkv][d/16][64] 16-byte MFMA B operands of k_score
+  uint32_t* B;                // [U][Hkv][d/16 + d/64][64] 16-byte MFMA B operands and reference magnitudes
+  float* nconst;              // [U][Hq] the norm term's shift sum_f n_f r_f per query head
   uint64_t* part;             // [U][Hq][n_tiles][3] tile moments of k_score, set to kUnpublished here
   int32_t* next_tile;         // tile claim counter of k_score, cleared here
   uint32_t* hist;             // [U][Hkv][kBins] aggregate histograms of k_score, cleared here
@@ -108,9 +115,10 @@ struct ScoreArgs {
   KView k;
   int32_t n_units, n_max, hkv, group, sink, window, tile, n_tiles, agg_mode;
   const int32_t* len;
-  const uint32_t* B;          // [U][Hkv][d/16][64] 16-byte MFMA B operands, from k_coef
+  const uint32_t* B;          // [U][Hkv][d/16 + d/64][64] 16-byte MFMA B operands and reference magnitudes
+  const float* nconst;        // [U][Hq] the norm term's shift, added back to per-query-head scores
   float* raw;                 // [U][Hq][n_max], may be null
-  double* part;               // [U][Hq][n_tiles][3] tile moments (count, sum, sum of squares)
+  double* part;               // [U][Hq][n_tiles][3] tile moments (count, mean, sum of squared deviations)
   float* agg;                 // [U][Hkv][n_max]
   int32_t* next_tile;         // next tile to claim
   uint32_t* hist;             // [U][Hkv][kBins] histogram of the aggregates' linear bins
@@ -200,9 +208,9 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s);
 // Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
 // of one (unit, KV head) must be resident together for the moment exchange.
-int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile);
-// LDS bytes of one k_score workgroup for tiles of `tile` keys
-size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size);
+// LDS bytes of one k_score workgroup for tiles of `tile` keys (block_size: of a paged cache)
+size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int block_size);
 // strategy: 0 automatic, 1 per group (when n_max fits), 2 tiled
 hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);

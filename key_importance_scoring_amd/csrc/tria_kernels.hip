@@ -127,6 +127,8 @@ struct Shape {
   static constexpr int NKC = D / 32;    // chunks per lane = MFMAs of the dot part
   static constexpr int NQ = D / 8;      // bands per lane
   static constexpr int NNC = D / 64;    // MFMAs per norm part
+  static constexpr int NR = D / 64;     // 16-byte slots of a lane's reference magnitudes (NQ bf16)
+  static constexpr int NBT = NKC + 2 * NNC + NR;   // 16-byte operands per lane written by k_coef
 };
 
 template <int D>
@@ -135,11 +137,13 @@ __device__ inline int chunk_elem(int i, int c) {
   return (i / HC) * (D / 2) + c * (D / 8) + (i % HC) * 8;
 }
 
+// The band a lane's q-th magnitude belongs to (the order band_sq forms them in).
 template <int D, int P>
 __device__ inline int lane_band(int q, int c) {
-  if (P == 0) return c * (D / 8) + q;                 // NEOX
-  if (q < D / 16) return c * (D / 16) + q;            // interleaved, first half
-  return D / 4 + c * (D / 16) + (q - D / 16);         // interleaved, second half
+  constexpr int HC = D / 64;
+  if (P == 0) return chunk_elem<D>(q / 8, c) + q % 8;                 // NEOX: real parts in chunks < HC
+  const int i = q < D / 16 ? q / 4 : HC + (q - D / 16) / 4;             // interleaved: (re, im) pairs
+  return chunk_elem<D>(i, c) / 2 + q % 4;
 }
 
 // ============================================================================ k_coef
@@ -177,12 +181,44 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   __shared__ float s_n[kMaxGroup * F];  // norm weights
   __shared__ double s_mur[kMaxGroup * F], s_mui[kMaxGroup * F], s_w[F];  // maximum over offsets
 
+  __shared__ float s_ref[F];            // reference magnitudes (bf16 values)
+  __shared__ float s_rsum[256];
+
   // blockIdx.z > 0 (the maximum over offsets only) writes a share of the offset
   // blocks' operands and nothing else
   const bool first = blockIdx.z == 0;
+  const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
+  // Reference magnitudes of the norm term: r_f = the mean |k_f| over kRefRows slots
+  // spread over the unit's keys.  The score kernel forms sum_f n_f (|k_f| - r_f) and
+  // the constant sum_f n_f r_f is added back only where per-query-head scores are
+  // written: the z-score does not change under a constant shift, and the bf16 hi/lo
+  // operands then carry each key's deviation from the reference, not its whole
+  // magnitude (so the error of a score stays small against the spread of the
+  // scores even when the norm term dominates their mean).  Any r_f gives the same
+  // scores in exact arithmetic.  Loaded first: they overlap the statistics' loads.
+  float rsum = 0.0f;
+  {
+    constexpr int subs = 256 / F, RPT = kRefRows / subs;   // sample rows per thread
+    const int f = t % F, sub = t / F;
+    if (first && n_u > 0) {
+      uint32_t re[RPT], im[RPT];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {   // every row's loads at once
+        const int r = sub + subs * i;
+        const int slot = (int)(((2 * (int64_t)r + 1) * n_u) / (2 * kRefRows));
+        const uint16_t* row = row_ptr(a.k, u, g, slot, nullptr);
+        re[i] = row ? row[P == 0 ? f : 2 * f] : 0u;
+        im[i] = row ? row[P == 0 ? f + F : 2 * f + 1] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float x = __uint_as_float(re[i] << 16), y = __uint_as_float(im[i] << 16);
+        rsum += sqrtf(x * x + y * y);
+      }
+    }
+  }
   // tiles past len[u] hold no keys: their moments are published here, as zeros
   if (first) {
-    const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
     const int64_t per = (int64_t)G * a.n_tiles * 3;
     for (int64_t i = t; i < per; i += 256) {
       const int tile = (int)((i / 3) % a.n_tiles);
@@ -257,14 +293,43 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     }
   }
   if (a.omax && t < F) s_w[t] = w;
+  s_rsum[t] = rsum;
   __syncthreads();
+  if (t < F) {
+    float r = 0.0f;
+    for (int j = 0; j < 256 / F; ++j) r += s_rsum[j * F + t];
+    r *= 1.0f / (float)kRefRows;
+    s_ref[t] = bf_lo(pack_bf16(r, 0.0f));   // the bf16 value the operands carry
+  }
+  __syncthreads();
+  // the constant each query head's norm term was shifted by: sum_f n_f r_f (fp64)
+  if (first) {
+    const int lane = t & 63, wave = t >> 6;
+    for (int h = wave; h < G; h += 4) {
+      double c = 0.0;
+      for (int f = lane; f < F; f += 64) c += (double)s_n[h * F + f] * (double)s_ref[f];
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+      if (lane == 0) a.nconst[(size_t)u * hq + g * G + h] = (float)c;
+    }
+  }
 
   // B operands: operand s of lane l at B[(u, g)][s][l]; s < NKC are the dot part's
-  // chunks, then the norm part's hi-magnitude and lo-magnitude operands
-  u32x4* dst = reinterpret_cast<u32x4*>(a.B) + ug * NB * 64;
-  for (int q = first ? t : NB * 64; q < NB * 64; q += 256) {
+  // chunks, then the norm part's hi-magnitude and lo-magnitude operands, then the
+  // lane's reference magnitudes (bf16 pairs, in the order band_sq forms its bands)
+  u32x4* dst = reinterpret_cast<u32x4*>(a.B) + ug * S::NBT * 64;
+  for (int q = first ? t : S::NBT * 64; q < S::NBT * 64; q += 256) {
     const int s = q / 64, lane = q % 64;
     const int col = lane & 15, grp = lane >> 4;
+    if (s >= NB) {
+      u32x4 w4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qb = 8 * (s - NB) + 2 * j;    // the lane's bands qb, qb + 1
+        w4[j] = pack_bf16(s_ref[lane_band<D, P>(qb, grp)], s_ref[lane_band<D, P>(qb + 1, grp)]);
+      }
+      dst[s * 64 + lane] = w4;
+      continue;
+    }
     int head = -1;
     bool lo = false;
     if (col < G) head = col;
@@ -456,11 +521,77 @@ __device__ inline void tile_len(const ScoreArgs& a, TileInfo& ti, int n_loaded, 
   ti.tlen = max(0, min(a.tile, ti.n - ti.tile0));
 }
 
-// Scores one tile into LDS (s_raw, [G][tile + 16]), writes the per-query-head
-// scores if wanted, and publishes the tile's candidate moments.
+// Registers a tile carries from tile_begin into tile_body: the wave's first stage of
+// keys, the (unit, KV head)'s MFMA B operands and the unit's length as loaded.
+template <int D, bool MAXO>
+struct TileRegs {
+  Stage<D, MAXO> cA;
+  bf16x8 bdot[D / 32], bna[D / 64], bnb[D / 64];
+  u32x4 rref[D / 64];   // the lane's reference magnitudes, bf16 pairs
+  int n_loaded;
+  int page0;
+};
+
+// Starts a tile: its block ids (paged caches) into LDS, then the loads of the B
+// operands and of every wave's first stage of keys, issued before len[u] is known.
+// Returns with those loads in flight, so that the work that follows (the previous
+// tile's moments and finalisation) overlaps them.
 template <int D, int P, bool PAGED, bool MAXO>
-__device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known, float* s_raw, int* s_bt,
-                                   u32x4* s_bmax, int* s_bug) {
+__device__ inline void tile_begin(const ScoreArgs& a, const TileInfo& ti, int n_known, int* s_bt,
+                                  TileRegs<D, MAXO>& r) {
+  using S = Shape<D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int kpw = a.tile / 4;      // keys per wave
+  const int u = ti.u, g = ti.g, tile0 = ti.tile0;
+  const int kw0 = tile0 + wave * kpw;
+  const int kw1 = kw0 + kpw;
+  // the slots the first stage may read: up to len[u] when it is known (n_known >= 0);
+  // else up to n_max (a dense view is readable, and a paged view's table covers, n_max
+  // slots), so that the first stage is issued before len[u] arrives
+  const int kcap = max(min(kw1, n_known >= 0 ? n_known : a.n_max), min(kw0 + 1, a.n_max));
+  r.n_loaded = n_known >= 0 ? n_known : a.len[u];
+
+  // ---- paged caches: the tile's block ids in LDS.  Ids of pages past len[u] may be
+  // anything: load_stage maps an out-of-pool id to block 0, and only pages that
+  // hold cached slots are checked (tile_body)
+  r.page0 = 0;
+  if (PAGED) {
+    r.page0 = tile0 / a.k.bs;
+    const int npcap = (min(tile0 + a.tile, a.n_max) - 1) / a.k.bs - r.page0 + 1;  // tile0 < n_max
+    for (int i = threadIdx.x; i < npcap; i += 256) s_bt[i] = a.k.bt[(int64_t)u * a.k.mb + r.page0 + i];
+    __syncthreads();
+  }
+
+  // ---- B operands of this lane's column, in the order k_coef wrote them
+  {
+    constexpr int NB = S::NKC + 2 * S::NNC;
+    const u32x4* bsrc = reinterpret_cast<const u32x4*>(a.B) + (size_t)ti.ug * S::NBT * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < S::NKC; ++i) r.bdot[i] = __builtin_bit_cast(bf16x8, bsrc[i * 64]);
+#pragma unroll
+    for (int i = 0; i < S::NNC; ++i) {
+      r.bna[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + i) * 64]);
+      r.bnb[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + S::NNC + i) * 64]);
+    }
+    if constexpr (!MAXO) {
+#pragma unroll
+      for (int i = 0; i < S::NR; ++i) r.rref[i] = bsrc[(NB + i) * 64];
+    }
+  }
+
+  // the first stage, unconditionally: a wave with no keys reloads row kcap - 1, which
+  // is below n_max and at or past tile0
+  load_stage<D, PAGED, MAXO>(r.cA, a.k, u, g, kw0, kcap, col, grp, s_bt, r.page0);
+}
+
+// Scores a started tile into LDS (s_raw, [G][tile + 16]); ends with a barrier, the
+// tile's scores complete in LDS.
+template <int D, int P, bool PAGED, bool MAXO>
+__device__ inline void tile_body(const ScoreArgs& a, TileInfo& ti, float* s_raw, const int* s_bt, u32x4* s_bmax,
+                                 int* s_bug, TileRegs<D, MAXO>& r) {
   using S = Shape<D>;
   constexpr int NBI = stage_blocks<D, MAXO>();
   constexpr int STAGE = 16 * NBI;  // keys per pipeline stage
@@ -469,46 +600,27 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int G = a.group;
-  const int hq = a.hkv * G;
   const int RS = a.tile + 16;      // LDS row stride: heads start 16 banks apart
   const int kpw = a.tile / 4;      // keys per wave
   const int u = ti.u, g = ti.g, tile0 = ti.tile0;
   const int kw0 = tile0 + wave * kpw;
-  // the slots the first stage may read: up to len[u] when it is known (n_known >= 0);
-  // else up to n_max (a dense view is readable, and a paged view's table covers, n_max
-  // slots), so that the first stage is issued before len[u] arrives
-  const int kcap = max(min(kw0 + kpw, n_known >= 0 ? n_known : a.n_max), min(kw0 + 1, a.n_max));
-  const int n_loaded = n_known >= 0 ? n_known : a.len[u];
-
-  // ---- paged caches: the tile's block ids in LDS.  Ids of pages past len[u] may be
-  // anything: load_stage maps an out-of-pool id to block 0, and only pages that
-  // hold cached slots are checked (below)
-  int page0 = 0;
-  if (PAGED) {
-    page0 = tile0 / a.k.bs;
-    const int npcap = (min(tile0 + a.tile, a.n_max) - 1) / a.k.bs - page0 + 1;  // tile0 < n_max
-    for (int i = threadIdx.x; i < npcap; i += 256) s_bt[i] = a.k.bt[(int64_t)u * a.k.mb + page0 + i];
-    __syncthreads();
-  }
-
-  // ---- B operands of this lane's column, in the order k_coef wrote them
-  bf16x8 bdot[S::NKC], bna[S::NNC], bnb[S::NNC];
-  {
-    constexpr int NB = S::NKC + 2 * S::NNC;
-    const u32x4* bsrc = reinterpret_cast<const u32x4*>(a.B) + (size_t)ti.ug * NB * 64 + lane;
-#pragma unroll
-    for (int i = 0; i < S::NKC; ++i) bdot[i] = __builtin_bit_cast(bf16x8, bsrc[i * 64]);
-#pragma unroll
-    for (int i = 0; i < S::NNC; ++i) {
-      bna[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + i) * 64]);
-      bnb[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + S::NNC + i) * 64]);
-    }
-  }
-
-  // the first stage, unconditionally and possibly before len[u] is known: a wave with
-  // no keys reloads row kcap - 1, which is below n_max and at or past tile0
-  Stage<D, MAXO> cA, cB;
-  load_stage<D, PAGED, MAXO>(cA, a.k, u, g, kw0, kcap, col, grp, s_bt, page0);
+  const int page0 = r.page0;
+  Stage<D, MAXO>& cA = r.cA;
+  Stage<D, MAXO> cB;
+  const bf16x8(&bdot)[S::NKC] = r.bdot;
+  const bf16x8(&bna)[S::NNC] = r.bna;
+  const bf16x8(&bnb)[S::NNC] = r.bnb;
+  // |k_f| - r_f for the lane's q-th band (the reference packed two per word; the
+  // maximum over offsets, whose score loop has no registers to spare, keeps the
+  // lane's references in LDS after its staged offset blocks)
+  const u32x4* s_rref = s_bmax + a.ob.nblk * S::NKC * 64;
+  auto mag = [&](const u32x4 (&ch)[D / 32], int q) {
+    const float m = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch, q));
+    uint32_t w;
+    if constexpr (MAXO) w = s_rref[(q / 8) * 64 + lane][(q % 8) / 2];
+    else w = r.rref[q / 8][(q % 8) / 2];
+    return m - ((q & 1) ? bf_hi(w) : bf_lo(w));
+  };
 
   // maximum over offsets: the (unit, KV head)'s offset blocks into LDS, unless the
   // previous tile of this workgroup already staged them (its reads have ended at the
@@ -517,6 +629,13 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     if (*s_bug != ti.ug) {
       const int nq = a.ob.nblk * S::NKC * 64;
       const u32x4* src = reinterpret_cast<const u32x4*>(a.Bmax) + (size_t)ti.ug * nq;
+      // the lane's reference magnitudes after the blocks (from k_coef's operands)
+      if (threadIdx.x < 64) {
+        constexpr int NB = S::NKC + 2 * S::NNC;
+        const u32x4* rsrc = reinterpret_cast<const u32x4*>(a.B) + (size_t)ti.ug * S::NBT * 64 + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < S::NR; ++i) s_bmax[nq + i * 64 + threadIdx.x] = rsrc[(NB + i) * 64];
+      }
       for (int q0 = 0; q0 < nq; q0 += 256 * 8) {
         u32x4 tmp[8];
 #pragma unroll
@@ -535,7 +654,7 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     }
   }
 
-  tile_len(a, ti, n_loaded, true);
+  tile_len(a, ti, r.n_loaded, true);
   const int n = ti.n;
   if (PAGED) {
     const int last = min(tile0 + a.tile, n) - 1;
@@ -569,8 +688,8 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
         u32x4 h4, l4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float m0 = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch[b], 8 * i + 2 * j));
-          const float m1 = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch[b], 8 * i + 2 * j + 1));
+          const float m0 = mag(ch[b], 8 * i + 2 * j);
+          const float m1 = mag(ch[b], 8 * i + 2 * j + 1);
           uint32_t hi, lw;
           split_bf16(m0, m1, hi, lw);
           h4[j] = hi;
@@ -652,8 +771,8 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
         u32x4 h4, l4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float m0 = __builtin_amdgcn_sqrtf(band_sq<D, P>(blk(bb), 8 * i + 2 * j));
-          const float m1 = __builtin_amdgcn_sqrtf(band_sq<D, P>(blk(bb), 8 * i + 2 * j + 1));
+          const float m0 = mag(blk(bb), 8 * i + 2 * j);
+          const float m1 = mag(blk(bb), 8 * i + 2 * j + 1);
           uint32_t hi, lw;
           split_bf16(m0, m1, hi, lw);
           h4[j] = hi;
@@ -700,18 +819,36 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     }
   }
   __syncthreads();
+}
+
+// The end of a scored tile (lengths filled by tile_body): its per-query-head scores
+// (if wanted) and its candidate moments (count, mean, sum of squared deviations),
+// published for the other tiles of its (unit, KV head).
+__device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const float* s_raw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = a.group;
+  const int hq = a.hkv * G;
+  const int RS = a.tile + 16;
+  const int u = ti.u, g = ti.g, tile0 = ti.tile0;
+  const int n = ti.n;
 
   // ---- per-query-head scores, if the caller wants them: full lines per head
   const int tlen = ti.tlen;
+  // (the tile's scores in LDS are shifted by the head's norm constant; added back here)
   if (a.raw) {
     for (int h = 0; h < G; ++h) {
       float* dst = a.raw + ((size_t)u * hq + g * G + h) * a.n_max + tile0;
       const float* src = s_raw + h * RS;
+      const float c = a.nconst[(size_t)u * hq + g * G + h];
       for (int i = 4 * threadIdx.x; i < tlen; i += 4 * 256) {
         if (i + 3 < tlen) {
-          *reinterpret_cast<f32x4*>(dst + i) = *reinterpret_cast<const f32x4*>(src + i);
+          f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] += c;
+          *reinterpret_cast<f32x4*>(dst + i) = v;
         } else {
-          for (int t = i; t < tlen; ++t) dst[t] = src[t];
+          for (int t = i; t < tlen; ++t) dst[t] = src[t] + c;
         }
       }
     }
@@ -755,20 +892,35 @@ __device__ inline void score_phase(const ScoreArgs& a, TileInfo ti, int n_known,
     for (int o = 32; o > 0; o >>= 1) m2 += __shfl_xor(m2, o);
     // pass-two deviations are about mf (the mean rounded to fp32): shift back
     const double dm = mean - (double)mf;
-    m2 -= (double)cnt * dm * dm;
+    m2 = fmax(m2 - (double)cnt * dm * dm, 0.0);
     if (lane == 0) {
       unsigned long long* p =
           reinterpret_cast<unsigned long long*>(a.part + (((size_t)u * hq + g * G + h) * a.n_tiles + ti.tile) * 3);
       __hip_atomic_store(p + 0, (unsigned long long)__double_as_longlong((double)cnt), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p + 1, (unsigned long long)__double_as_longlong(sum), __ATOMIC_RELAXED,
+      __hip_atomic_store(p + 1, (unsigned long long)__double_as_longlong(mean), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p + 2, (unsigned long long)__double_as_longlong(m2 + (double)cnt * mean * mean),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p + 2, (unsigned long long)__double_as_longlong(m2), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   // nothing waits for these stores: each moment is a single-copy-atomic 8-byte
   // store, and a reader takes it as published once it no longer reads kUnpublished
+}
+
+// Adds the moments (nb, mb, M2b) of a set of scores to the running (n, m, M2):
+// count, mean and sum of squared deviations of the union (the pairwise update of
+// Chan, Golub and LeVeque).  An empty set (nb = 0) changes nothing; an empty running
+// set takes the other's moments as they are.
+__device__ inline void chan_merge(double& n, double& m, double& M2, double nb, double mb, double M2b) {
+  const double nt = n + nb;
+  if (nt > 0.0) {
+    const double d = mb - m;
+    const double f = nb / nt;
+    m += d * f;
+    M2 += M2b + d * d * n * f;
+  }
+  n = nt;
 }
 
 // Waits until every tile of the (unit, KV head) of `ti` has published its moments,
@@ -787,23 +939,23 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
   tile_len(a, ti, n_known >= 0 ? n_known : a.len[ti.u], false);
 
   // the group's mean and standard deviation per query head, from every tile's
-  // moments (fixed summation order: lane j takes tiles j, j + 64, ...; then a fixed
-  // shuffle tree); a wave polls until none of its head's moments reads kUnpublished
+  // (count, mean, M2) by the pairwise update of Chan, Golub and LeVeque (no
+  // difference of large sums), in a fixed order: lane j merges tiles j, j + 64, ...
+  // in turn, then a fixed shuffle tree merges the lanes.  A wave polls until none of
+  // its head's moments reads kUnpublished.
   for (int h = wave; h < G; h += 4) {
     const unsigned long long* p =
         reinterpret_cast<const unsigned long long*>(a.part + ((size_t)ti.u * hq + ti.g * G + h) * a.n_tiles * 3);
-    double c, s1, s2;
+    double c, m, m2;
     for (int polls = 0;; ++polls) {
-      c = s1 = s2 = 0.0;
+      c = m = m2 = 0.0;
       bool missing = false;
       for (int j = lane; j < a.n_tiles; j += 64) {
         const unsigned long long x0 = __hip_atomic_load(p + 3 * j + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned long long x1 = __hip_atomic_load(p + 3 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned long long x2 = __hip_atomic_load(p + 3 * j + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         missing |= (x0 == kUnpublished) | (x1 == kUnpublished) | (x2 == kUnpublished);
-        c += __longlong_as_double(x0);
-        s1 += __longlong_as_double(x1);
-        s2 += __longlong_as_double(x2);
+        chan_merge(c, m, m2, __longlong_as_double(x0), __longlong_as_double(x1), __longlong_as_double(x2));
       }
       if (__ballot(missing) == 0) break;
       if (polls >= kPollLimit) {
@@ -813,14 +965,12 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
       __builtin_amdgcn_s_sleep(8);
     }
     for (int o = 32; o > 0; o >>= 1) {
-      c += __shfl_xor(c, o);
-      s1 += __shfl_xor(s1, o);
-      s2 += __shfl_xor(s2, o);
+      const double oc = __shfl_xor(c, o), om = __shfl_xor(m, o), om2 = __shfl_xor(m2, o);
+      chan_merge(c, m, m2, oc, om, om2);
     }
     if (lane == 0) {
-      const double m = c > 0.0 ? s1 / c : 0.0;
-      const double var = c > 0.0 ? fmax(s2 / c - m * m, 0.0) : 0.0;
-      s_mean[h] = (float)m;
+      const double var = c > 0.0 ? fmax(m2 / c, 0.0) : 0.0;
+      s_mean[h] = (float)(c > 0.0 ? m : 0.0);
       s_inv[h] = (float)(1.0 / fmax(sqrt(var), 1e-12));
     }
   }
@@ -867,6 +1017,16 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
   }
 }
 
+// Block ids a score tile of `tile` slots can touch in a paged cache of block size bs.
+__host__ __device__ inline int tile_pages(int tile, int bs) { return (tile + bs - 1) / bs + 1; }
+
+// 32-bit words of the score kernel's LDS region shared by a tile's block ids (paged)
+// and the finalisation's histogram (the mean over offsets only).
+__host__ __device__ inline int score_scratch(bool omax, bool paged, int tile, int bs) {
+  const int pages = paged ? tile_pages(tile, bs) : 0;
+  return omax ? pages : (pages > kBins ? pages : kBins);
+}
+
 // Persistent score kernel: as many workgroups as fit on the device claim tiles in
 // order from a counter.  Each workgroup scores and publishes its current tile, and
 // only then finalises its previous one (two LDS score buffers): by that time the
@@ -879,6 +1039,11 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
 // wait; with P workgroups each holding at most two tiles, a circular wait would
 // need 2P <= n_tiles, and P >= n_tiles (the host checks it), so the wait always ends
 // (it is also bounded, and flagged, as a last resort).
+//
+// (Measured and dropped: claiming the next tile and issuing its first loads before
+// the previous tile's finalisation, and two other key layouts over the waves: none
+// changed the score kernel's time on the Qwen3-8B-shaped cache by more than 2 %, the
+// first made it 2 % slower.)
 template <int D, int P, bool PAGED, bool MAXO>
 __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
   extern __shared__ float s_dyn[];
@@ -888,15 +1053,17 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
   const int RS = a.tile + 16;
   float* buf0 = s_dyn;
   float* buf1 = s_dyn + G * RS;
+  // LDS after the two score buffers: one region for the tile's block ids (paged)
+  // and the finalisation's histogram (they are never live together; the maximum over
+  // offsets keeps the histogram in the staged offset blocks' region instead, restaged
+  // after every finalisation), the units' lengths and tile prefix, the staged offset
+  // blocks (the maximum over offsets)
+  const int scratch = score_scratch(MAXO, PAGED, a.tile, a.k.bs);
   int* s_bt = reinterpret_cast<int*>(s_dyn + 2 * G * RS);
-  // the mean: one region for the tile's block ids (paged) and the finalisation's
-  // histogram; the maximum over offsets: the block ids only, the histogram shares
-  // the staged offset blocks' region (restaged after every finalisation)
-  const int scratch = MAXO ? (PAGED ? a.tile + 1 : 0) : (PAGED && a.tile + 1 > kBins ? a.tile + 1 : kBins);
   int* s_len = s_bt + scratch;            // [kListUnits] lengths
   int* s_pre = s_len + kListUnits;        // [kListUnits + 1] tiles of the units before
-  // maximum over offsets: the staged offset blocks, 16-byte aligned
-  u32x4* s_bmax = reinterpret_cast<u32x4*>(s_dyn + ((2 * G * RS + scratch + 2 * kListUnits + 1 + 3) & ~3));
+  const int used = 2 * G * RS + scratch + 2 * kListUnits + 1;
+  u32x4* s_bmax = reinterpret_cast<u32x4*>(s_dyn + ((used + 3) & ~3));   // 16-byte aligned
   uint32_t* s_hist = MAXO ? reinterpret_cast<uint32_t*>(s_bmax) : reinterpret_cast<uint32_t*>(s_bt);
   if (threadIdx.x == 0) s_bug = -1;
   const int U = a.n_units;
@@ -931,50 +1098,57 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
     total = s_pre[U];
   }
   // claim index -> (unit x KV head, tile)
-  auto place = [&](int t, int& ug, int& tile) {
+  auto place = [&](int t) {
+    int ug, tile;
     if (!listed) {
       tile = t % a.n_tiles;
       ug = t / a.n_tiles;
-      return;
+    } else {
+      int lo = 0, hi = U - 1;   // the last unit whose tiles start at or before t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int r = t - s_pre[lo];
+      const int nt = (s_len[lo] + a.tile - 1) / a.tile;
+      ug = lo * a.hkv + r / nt;
+      tile = r % nt;
     }
-    int lo = 0, hi = U - 1;   // the last unit whose tiles start at or before t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pre[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int r = t - s_pre[lo];
-    const int nt = (s_len[lo] + a.tile - 1) / a.tile;
-    ug = lo * a.hkv + r / nt;
-    tile = r % nt;
+    return tile_info(a, ug, tile);
   };
-  int pug = -1, ptile = 0;
-  bool b = false;
+  auto known_len = [&](const TileInfo& ti) { return listed ? s_len[ti.u] : -1; };
+
+  TileRegs<D, MAXO> regs;
+  TileInfo prev{};
+  bool have_prev = false, b = false;
   for (;;) {
     if (threadIdx.x == 0) s_t = atomicAdd(a.next_tile, 1);
     __syncthreads();
     const int t = s_t;
     __syncthreads();
-    int ug = 0, tile = 0;
+    TileInfo cur{};
     if (t < total) {
-      place(t, ug, tile);
-      score_phase<D, P, PAGED, MAXO>(a, tile_info(a, ug, tile), listed ? s_len[ug / a.hkv] : -1, b ? buf1 : buf0,
-                                     s_bt, s_bmax, &s_bug);
+      cur = place(t);
+      float* sbuf = b ? buf1 : buf0;
+      tile_begin<D, P, PAGED, MAXO>(a, cur, known_len(cur), s_bt, regs);
+      tile_body<D, P, PAGED, MAXO>(a, cur, sbuf, s_bt, s_bmax, &s_bug, regs);   // ends with a barrier
+      tile_end(a, cur, sbuf);
     }
-    // s_bt (or, for the maximum over offsets, the offset blocks) served the current
-    // tile's score phase; finalize reuses it as histogram scratch
-    if (pug >= 0) {
-      finalize_tile(a, tile_info(a, pug, ptile), listed ? s_len[pug / a.hkv] : -1, b ? buf0 : buf1, s_hist);
+    // finalize uses the histogram region (for the maximum over offsets, the staged
+    // offset blocks' region, restaged for the next tile)
+    if (have_prev) {
+      finalize_tile(a, prev, known_len(prev), b ? buf0 : buf1, s_hist);
       if (MAXO && threadIdx.x == 0) s_bug = -1;
     }
     if (t >= total) break;
-    pug = ug;
-    ptile = tile;
+    prev = cur;
+    have_prev = true;
     b = !b;
   }
 }
 
 template <int D, int P, bool PAGED>
-__global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score(ScoreArgs a) {
   score_kernel<D, P, PAGED, false>(a);
 }
 
@@ -1875,23 +2049,20 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile) {
-  // two score buffers, a region that holds the tile's block ids during the score
-  // phase and (the mean) the aggregate histogram during finalisation, the units'
-  // lengths and tile prefix, and for the maximum over offsets the staged offset
-  // blocks, which share their region with the histogram
-  if (!omax) {
-    const size_t scratch = paged && tile + 1 > kBins ? (size_t)tile + 1 : (size_t)kBins;
-    return ((size_t)2 * group * (tile + 16) + scratch + (size_t)(2 * kListUnits + 1)) * 4;
-  }
-  const size_t scratch = paged ? (size_t)tile + 1 : 0;
-  const size_t base = (size_t)2 * group * (tile + 16) + scratch + (size_t)(2 * kListUnits + 1);
-  const size_t blocks = (size_t)nblk * (d / 32) * 64 * 16;
-  return ((base + 3) & ~(size_t)3) * 4 + (blocks > (size_t)kBins * 4 ? blocks : (size_t)kBins * 4);
+size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int block_size) {
+  // two score buffers, the region shared by the tile's block ids and (the mean) the
+  // finalisation's histogram, the units' lengths and tile prefix, and for the maximum
+  // over offsets the staged offset blocks, whose region also holds the histogram
+  const size_t used = (size_t)2 * group * (tile + 16) + (size_t)score_scratch(omax, paged, tile, block_size) +
+                      (size_t)(2 * kListUnits + 1);
+  if (!omax) return used * 4;
+  // the blocks, then the lanes' reference magnitudes (d/64 16-byte operands a lane)
+  const size_t blocks = (size_t)nblk * (d / 32) * 64 * 16 + (size_t)(d / 64) * 64 * 16;
+  return ((used + 3) & ~(size_t)3) * 4 + (blocks > (size_t)kBins * 4 ? blocks : (size_t)kBins * 4);
 }
 
-int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile) {
-  const size_t lds = score_lds(d, group, paged, omax, nblk, tile);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size) {
+  const size_t lds = score_lds(d, group, paged, omax, nblk, tile, block_size);
   int per_cu = 0, dev = 0, cus = 0;
   hipError_t e = hipErrorInvalidValue;
 #define TRIA_OCC_CASE(DD, PP, PG, MX)                                                                     \
@@ -1925,11 +2096,11 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
   const long tiles = (long)a.n_units * a.hkv * a.n_tiles;
   if (tiles == 0) return hipSuccess;
   const bool paged = a.k.bt != nullptr;
-  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk, a.tile);
+  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk, a.tile, a.k.bs);
   if (max_wg > 0 && max_wg < cap) cap = max_wg;
   if (cap < a.n_tiles) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
-  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk, a.tile);
+  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk, a.tile, a.k.bs);
 #define TRIA_SCORE_CASE(DD, PP, PG, MX)                                       \
   if (d == DD && pairing == PP && paged == PG && (a.omax != 0) == MX) {      \
     if (MX) hipLaunchKernelGGL((k_score_max<DD, PP, PG>), grid, blk, lds, s, a); \

@@ -11,7 +11,8 @@ Recipe (the same for every workload, see ``CONFIGS``):
 
 * key centre per (layer, KV head, band): ``c = r e^{i psi}``, ``r ~ U(0.5, 2)``,
   ``psi ~ U[0, 2 pi)``;  "non-concentrated" heads get ``r = 0``;
-* pre-rotation key band ``k_f = c_f + (x + i y)``, ``x, y ~ N(0, 0.3^2)``;
+* pre-rotation key band ``k_f = c_f + (x + i y)``, ``x, y ~ N(0, 0.3^2)`` (the std
+  is ``key_noise``, 0.3 in every workload);
 * the key is rotated at its position ``p`` (band f turned by ``p * theta^(-2f/d)``),
   laid out in the model's pairing (NEOX: re in dims ``[0, d/2)``, im in
   ``[d/2, d)``; interleaved: re in even dims, im in odd dims) and rounded to
@@ -20,7 +21,8 @@ Recipe (the same for every workload, see ``CONFIGS``):
 * query statistics per (layer, q-head, band): centre ``mu`` drawn like the key
   centre, ``E|q_f| = |mu_f| (1 + U(0, 0.5))``, stored as fp32; for the q-heads
   of a non-concentrated KV head ``mu`` is scaled by 1e-3 while ``E|q_f|`` keeps
-  an O(1) magnitude ``r (1 + U(0, 0.5))``, ``r ~ U(0.5, 2)``;
+  an O(1) magnitude ``r (1 + U(0, 0.5))``, ``r ~ U(0.5, 2)``; ``mu_scale`` (1 in
+  every workload) scales the other heads' ``mu`` after ``E|q_f|`` is drawn;
 * positions are ``0 .. len-1`` (a fresh cache) and the current query sits at
   ``len - 1``.
 
@@ -66,6 +68,8 @@ class Config:
     nonconc_frac: float = 0.0
     seed: int = 0
     offset_reduce: str = "mean"   # "mean" (the method) | "max": reduction over the future offsets
+    key_noise: float = 0.3        # std of each pre-rotation key component around the centre
+    mu_scale: float = 1.0         # scales the query centres E[q_f] only (E|q_f| is drawn unscaled)
 
     @property
     def n_q_heads(self) -> int:
@@ -211,6 +215,7 @@ def q_stats(cfg: Config):
                 mu = mu * 1e-3
             else:
                 absm = np.abs(mu) * spread
+                mu = mu * cfg.mu_scale
             re[l, h] = mu.real
             im[l, h] = mu.imag
             ab[l, h] = absm
@@ -252,7 +257,7 @@ def key_rows(cfg: Config, unit: int, kv_head: int) -> np.ndarray:
     F = cfg.head_dim // 2
     c = key_centres(cfg, layer, kv_head)
     rng = _rng(cfg, _K_NOISE, unit, kv_head)
-    noise = rng.standard_normal((2, n, F)) * 0.3
+    noise = rng.standard_normal((2, n, F)) * cfg.key_noise
     a = c.real[None, :] + noise[0]
     b = c.imag[None, :] + noise[1]
     cos, sin = _rotation(cfg.n_kv, cfg.head_dim, cfg.rope_base)
@@ -275,7 +280,7 @@ def decode_rows(cfg: Config, unit: int, kv_head: int, p0: int, count: int, which
     layer = int(units(cfg).unit_layer[unit])
     c = key_centres(cfg, layer, kv_head)
     rng = _rng(cfg, _DEC_K, unit * 4096 + kv_head, p0)
-    noise = rng.standard_normal((2, count, F)) * 0.3
+    noise = rng.standard_normal((2, count, F)) * cfg.key_noise
     a = c.real[None, :] + noise[0]
     b = c.imag[None, :] + noise[1]
     inv_freq = cfg.rope_base ** (-(2.0 * np.arange(F, dtype=np.float64)) / cfg.head_dim)

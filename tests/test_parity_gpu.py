@@ -39,6 +39,13 @@ SMALL = {
     "all_protected": C["tiny"].replace(name="all_protected", n_kv=200, window=256, budget=300),
     "short_units": C["batched_decode"].replace(name="short_units", n_seqs=5, n_kv=40, ragged_min=1, window=8,
                                               sink=2, budget_frac=0.5),
+    # scores whose mean is over 10^3 standard deviations: tightly concentrated keys,
+    # query centres 10^-4 of E|q_f| (the norm term dominates the score); the moments and
+    # the norm term's operands must keep the z-scores to the tolerance
+    "concentrated": C["qwen3_8b"].replace(name="concentrated", n_layers=2, n_kv=5003, budget=1000,
+                                          key_noise=0.002, mu_scale=1e-4),
+    "concentrated_lc": C["long_context"].replace(name="concentrated_lc", n_kv=6000, budget=600, agg="mean",
+                                                 key_noise=0.002, mu_scale=1e-4),
     # more units than the score kernel keeps lengths of in LDS: every tile is claimed
     "many_units": C["batched_decode"].replace(name="many_units", n_seqs=520, n_kv_heads=2, n_kv=2200,
                                              ragged_min=16, window=64, budget_frac=0.4),
@@ -120,6 +127,8 @@ MAXO = {
                                     offset_reduce="max"),
     "g7_max": C["qwen3_8b"].replace(name="g7_max", n_layers=1, n_kv_heads=2, group=7, n_kv=2222, budget=800,
                                     agg="mean", offset_reduce="max"),
+    "concentrated_max": C["qwen3_8b"].replace(name="concentrated_max", n_layers=1, n_kv=3001, budget=700,
+                                              key_noise=0.002, mu_scale=1e-4, offset_reduce="max"),
 }
 
 
