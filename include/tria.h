@@ -85,9 +85,11 @@ enum {
   TRIA_FLAG_BLOCK = 8,   /* block id outside [0, n_pool_blocks): row skipped   */
   TRIA_FLAG_INDEX = 16,  /* compaction index outside [0, len[u]): row skipped  */
   TRIA_FLAG_BMAX = 32,   /* min(budget, len) > b_max: clamped to b_max         */
-  TRIA_FLAG_SYNC = 64    /* tria_score: a group of tiles did not all publish
-                            their moments within the bounded wait; the
-                            aggregates of that (unit, KV head) are unspecified */
+  TRIA_FLAG_SYNC = 64    /* tria_score, information only: a group's tiles did
+                            not all publish their moments within the bounded
+                            wait (or tria_score_wait_polls asked for no wait),
+                            and a workgroup computed that group's moments
+                            directly from the K cache; results remain valid  */
 };
 
 /* Shape and method parameters (a host struct, read during the call only). */
@@ -182,9 +184,11 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max)
  * (1024 for G > 4 or the maximum over offsets; balanced in multiples of 256 when
  * n_max is larger, e.g. 1280 + 896 for 2176) by
  * concurrent workgroups that exchange their tile moments through the workspace
- * and wait (boundedly) for one another before normalising; this relies on the
- * hardware dispatching a kernel's workgroups in order, and reports
- * TRIA_FLAG_SYNC instead of hanging if a wait ever expires.
+ * and wait (boundedly) for one another before normalising.  When a wait runs out
+ * (another stream's kernels holding compute units, say), the waiting workgroup
+ * scores the group's keys again and forms its moments itself, and TRIA_FLAG_SYNC
+ * records that this slower path ran: the results never depend on the tiles'
+ * workgroups being resident together.
  */
 tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
                        const int32_t* len, const int32_t* unit_layer, const int32_t* q_pos,
@@ -372,6 +376,16 @@ tria_status tria_stats_layer_budgets(int32_t n_units, const int32_t* unit_layer,
  * tile's arithmetic and every reduction run in a fixed order.  Process-wide;
  * returns the previous cap. */
 int32_t tria_score_max_workgroups(int32_t cap);
+
+/* Polls of tria_score's bounded wait for a group's tile moments (the default,
+ * 65536, is ~0.1-0.2 s).  When a wait runs out, the workgroup computes the group's
+ * moments directly from the K cache instead (TRIA_FLAG_SYNC is raised as
+ * information).  A negative value skips the exchange altogether: every
+ * finalisation computes its group's moments directly (each re-reads the group's
+ * keys: for tests of that path, not for speed).  Results agree with the exchange
+ * up to rounding.  Process-wide; returns the previous value.  For callers whose
+ * other streams keep compute units busy, and for tests. */
+int32_t tria_score_wait_polls(int32_t polls);
 
 /* How tria_select distributes its work.  Both strategies keep the same slots
  * (bit-identical idx and cnt).

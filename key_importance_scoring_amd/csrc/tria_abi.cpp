@@ -46,6 +46,7 @@ std::mutex g_tmu;
 bool g_timing = false;
 std::vector<Rec> g_recs;
 
+
 // Runs `launch` on `stream`, bracketed by HIP events on the same stream when
 // timing is on.  The events skip the system-scope fence (an L2 writeback and
 // invalidate) a default event performs on record; each recorded event still idles
@@ -78,6 +79,8 @@ tria_status launch_status(hipError_t e, const char* what) {
 
 // cap on tria_score's persistent grid (0: the device's resident capacity)
 std::atomic<int32_t> g_score_wg_cap{0};
+// polls of the score kernel's bounded wait for a group's moments (< 0: none)
+std::atomic<int32_t> g_wait_polls{tria::kPollLimit};
 // tria_select's work distribution (tria_select_strategy_t)
 std::atomic<int32_t> g_select_strategy{TRIA_SELECT_AUTO};
 
@@ -204,10 +207,16 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max)
   return layout(p, n_units, n_max).total;
 }
 
-tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
+}  // extern "C"
+
+namespace {
+
+// The bodies of the entry points: every check first; with dry = true nothing is
+// launched (tria_pass_noalloc validates all three steps before it launches any).
+tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
                        const int32_t* len, const int32_t* unit_layer, const int32_t* q_pos,
                        const float* q_mean_re, const float* q_mean_im, const float* q_abs_mean, float* raw,
-                       float* agg, void* ws, size_t ws_bytes, void* stream) {
+                       float* agg, void* ws, size_t ws_bytes, void* stream, bool dry) {
   tria_status st = check_params(p);
   if (st != TRIA_OK) return st;
   if (n_units < 0 || n_max < 0) return fail(TRIA_EINVAL, "n_units and n_max must be >= 0");
@@ -239,6 +248,7 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   if (wg_cap > 0 && L.n_tiles > wg_cap)
     return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the workgroup cap is %d",
                 n_max, L.n_tiles, wg_cap);
+  if (dry) return TRIA_OK;
 
   char* w = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -264,14 +274,14 @@ tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_un
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
                      L.tile, L.n_tiles, p->agg,
                      len, B, nconst, raw, part, agg, next_tile, hist, flags, omax,
-                     reinterpret_cast<const uint32_t*>(w + L.Bmax), L.ob};
+                     reinterpret_cast<const uint32_t*>(w + L.Bmax), L.ob, g_wait_polls.load()};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, wg_cap, s); });
   return launch_status(e, "k_score");
 }
 
-tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+tria_status select_impl(const tria_params* p, int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
                         const int32_t* budget, const float* agg, int32_t* idx, int32_t* cnt, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        size_t ws_bytes, void* stream, bool dry) {
   tria_status st = check_params(p);
   if (st != TRIA_OK) return st;
   if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
@@ -288,6 +298,7 @@ tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, in
   char* w = static_cast<char*>(ws);
   if (L.n_st > tria::kMaxSelTiles)
     return fail(TRIA_ESHAPE, "n_max %d exceeds the selection's %d tiles", n_max, tria::kMaxSelTiles);
+  if (dry) return TRIA_OK;
   int32_t* tiles = reinterpret_cast<int32_t*>(w + L.tiles);
   const size_t nt = (size_t)n_units * p->n_kv_heads * L.n_st;
   tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, L.n_st, len, budget, agg,
@@ -301,10 +312,10 @@ tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, in
   return launch_status(e, "k_select");
 }
 
-tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const tria_kv_view* v_src,
+tria_status compact_impl(const tria_params* p, const tria_kv_view* k_src, const tria_kv_view* v_src,
                          const int32_t* pos_src, int32_t pos_heads, int32_t n_units, int32_t n_max, int32_t b_max,
                          const int32_t* len, const int32_t* idx, const int32_t* cnt, const tria_kv_view* k_dst,
-                         const tria_kv_view* v_dst, int32_t* pos_dst, void* stream) {
+                         const tria_kv_view* v_dst, int32_t* pos_dst, void* stream, bool dry) {
   tria_status st = check_params(p);
   if (st != TRIA_OK) return st;
   if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
@@ -346,6 +357,7 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
     const uintptr_t d1 = d0 + (size_t)n_units * hkv * b_max * 4;
     if (overlaps(s0, s1, d0, d1)) return fail(TRIA_EOVERLAP, "pos_dst overlaps pos_src");
   }
+  if (dry) return TRIA_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t n_rtiles = (b_max + tria::kCompactRows - 1) / tria::kCompactRows;
@@ -353,6 +365,32 @@ tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const 
                        n_units, n_max, b_max, hkv, d, n_rtiles, len, idx, cnt, nullptr};
   hipError_t e = timed(kIdCompact, s, [&] { return tria::launch_compact(ca, s); });
   return launch_status(e, "k_compact");
+}
+
+}  // namespace
+
+extern "C" {
+
+tria_status tria_score(const tria_params* p, const tria_kv_view* k, int32_t n_units, int32_t n_max,
+                       const int32_t* len, const int32_t* unit_layer, const int32_t* q_pos,
+                       const float* q_mean_re, const float* q_mean_im, const float* q_abs_mean, float* raw,
+                       float* agg, void* ws, size_t ws_bytes, void* stream) {
+  return score_impl(p, k, n_units, n_max, len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, raw, agg, ws,
+                    ws_bytes, stream, false);
+}
+
+tria_status tria_select(const tria_params* p, int32_t n_units, int32_t n_max, int32_t b_max, const int32_t* len,
+                        const int32_t* budget, const float* agg, int32_t* idx, int32_t* cnt, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return select_impl(p, n_units, n_max, b_max, len, budget, agg, idx, cnt, ws, ws_bytes, stream, false);
+}
+
+tria_status tria_compact(const tria_params* p, const tria_kv_view* k_src, const tria_kv_view* v_src,
+                         const int32_t* pos_src, int32_t pos_heads, int32_t n_units, int32_t n_max, int32_t b_max,
+                         const int32_t* len, const int32_t* idx, const int32_t* cnt, const tria_kv_view* k_dst,
+                         const tria_kv_view* v_dst, int32_t* pos_dst, void* stream) {
+  return compact_impl(p, k_src, v_src, pos_src, pos_heads, n_units, n_max, b_max, len, idx, cnt, k_dst, v_dst,
+                      pos_dst, stream, false);
 }
 
 size_t tria_calibrate_workspace_size(const tria_params* p, int32_t n_tokens) {
@@ -468,6 +506,10 @@ int32_t tria_select_strategy(int32_t strategy) {
 
 int32_t tria_score_max_workgroups(int32_t cap) {
   return g_score_wg_cap.exchange(cap < 0 ? 0 : cap);
+}
+
+int32_t tria_score_wait_polls(int32_t polls) {
+  return g_wait_polls.exchange(polls < 0 ? -1 : polls);
 }
 
 int32_t tria_timing_enable(int32_t on) {

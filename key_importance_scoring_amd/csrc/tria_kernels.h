@@ -37,7 +37,8 @@ inline int score_tile_keys(int group, int omax, int n_max) {
 // take (NaNs that arithmetic produces keep an fp32 payload or are the default one).
 constexpr uint64_t kUnpublished = ~0ull;
 // Bounded wait for a group's tile moments: each poll is one memory round trip plus a
-// short sleep (~0.1-0.2 s in all).
+// short sleep (~0.1-0.2 s in all); when it runs out the group's moments are computed
+// directly from the K cache.
 constexpr int kPollLimit = 1 << 16;
 // Linear bins of an aggregate (a z-score: scale-free): 2048 bins over [-8, 8), one
 // below, one above, one for +inf (protected slots).
@@ -126,6 +127,7 @@ struct ScoreArgs {
   int32_t omax;               // 1: maximum over the offsets (B operands of the norm part still in B)
   const uint32_t* Bmax;       // omax: [U][Hkv][nblk][d/32][64] 16-byte B operands of the offset blocks
   OffsetBlocks ob;
+  int32_t wait_polls;         // polls of a finalisation's wait (< 0: compute the moments directly at once)
 };
 
 // Per-(unit, KV head) state of the selection, in the workspace.
@@ -243,5 +245,6 @@ struct AppendArgs {
   int32_t* flags;
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
 
 }  // namespace tria

@@ -196,24 +196,22 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   // magnitude (so the error of a score stays small against the spread of the
   // scores even when the norm term dominates their mean).  Any r_f gives the same
   // scores in exact arithmetic.  Loaded first: they overlap the statistics' loads.
-  float rsum = 0.0f;
+  constexpr int RPT = kRefRows / (256 / F);   // sample rows per thread
+  uint32_t ref_re[RPT], ref_im[RPT];            // consumed after the twiddles: the loads overlap them
   {
-    constexpr int subs = 256 / F, RPT = kRefRows / subs;   // sample rows per thread
+    constexpr int subs = 256 / F;
     const int f = t % F, sub = t / F;
-    if (first && n_u > 0) {
-      uint32_t re[RPT], im[RPT];
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {   // every row's loads at once
+    for (int i = 0; i < RPT; ++i) {
+      ref_re[i] = ref_im[i] = 0u;
+      if (first && n_u > 0) {
         const int r = sub + subs * i;
         const int slot = (int)(((2 * (int64_t)r + 1) * n_u) / (2 * kRefRows));
         const uint16_t* row = row_ptr(a.k, u, g, slot, nullptr);
-        re[i] = row ? row[P == 0 ? f : 2 * f] : 0u;
-        im[i] = row ? row[P == 0 ? f + F : 2 * f + 1] : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float x = __uint_as_float(re[i] << 16), y = __uint_as_float(im[i] << 16);
-        rsum += sqrtf(x * x + y * y);
+        if (row) {
+          ref_re[i] = row[P == 0 ? f : 2 * f];
+          ref_im[i] = row[P == 0 ? f + F : 2 * f + 1];
+        }
       }
     }
   }
@@ -293,7 +291,15 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     }
   }
   if (a.omax && t < F) s_w[t] = w;
-  s_rsum[t] = rsum;
+  {
+    float rsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float x = __uint_as_float(ref_re[i] << 16), y = __uint_as_float(ref_im[i] << 16);
+      rsum += sqrtf(x * x + y * y);
+    }
+    s_rsum[t] = rsum;
+  }
   __syncthreads();
   if (t < F) {
     float r = 0.0f;
@@ -614,13 +620,12 @@ __device__ inline void tile_body(const ScoreArgs& a, TileInfo& ti, float* s_raw,
   // maximum over offsets, whose score loop has no registers to spare, keeps the
   // lane's references in LDS after its staged offset blocks)
   const u32x4* s_rref = s_bmax + a.ob.nblk * S::NKC * 64;
-  auto mag = [&](const u32x4 (&ch)[D / 32], int q) {
+  auto mag_ref = [&](const u32x4 (&ch)[D / 32], int q, const u32x4 (&rr)[S::NR]) {
     const float m = __builtin_amdgcn_sqrtf(band_sq<D, P>(ch, q));
-    uint32_t w;
-    if constexpr (MAXO) w = s_rref[(q / 8) * 64 + lane][(q % 8) / 2];
-    else w = r.rref[q / 8][(q % 8) / 2];
+    const uint32_t w = rr[q / 8][(q % 8) / 2];
     return m - ((q & 1) ? bf_hi(w) : bf_lo(w));
   };
+  auto mag = [&](const u32x4 (&ch)[D / 32], int q) { return mag_ref(ch, q, r.rref); };
 
   // maximum over offsets: the (unit, KV head)'s offset blocks into LDS, unless the
   // previous tile of this workgroup already staged them (its reads have ended at the
@@ -762,7 +767,11 @@ __device__ inline void tile_body(const ScoreArgs& a, TileInfo& ti, float* s_raw,
           best[bb][t] = __builtin_elementwise_maximum(best[bb][t], __int_as_float(y));
         }
     }
-    // the norm term (no offset), hi + lo merged into the owner lanes as well
+    // the norm term (no offset), hi + lo merged into the owner lanes as well; the
+    // lane's references from LDS, once for all the blocks
+    u32x4 rr[S::NR];
+#pragma unroll
+    for (int i = 0; i < S::NR; ++i) rr[i] = s_rref[i * 64 + lane];
 #pragma unroll
     for (int bb = 0; bb < NB2; ++bb) {
       f32x4 nrm = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -771,8 +780,8 @@ __device__ inline void tile_body(const ScoreArgs& a, TileInfo& ti, float* s_raw,
         u32x4 h4, l4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float m0 = mag(blk(bb), 8 * i + 2 * j);
-          const float m1 = mag(blk(bb), 8 * i + 2 * j + 1);
+          const float m0 = mag_ref(blk(bb), 8 * i + 2 * j, rr);
+          const float m1 = mag_ref(blk(bb), 8 * i + 2 * j + 1, rr);
           uint32_t hi, lw;
           split_bf16(m0, m1, hi, lw);
           h4[j] = hi;
@@ -923,11 +932,177 @@ __device__ inline void chan_merge(double& n, double& m, double& M2, double nb, d
   n = nt;
 }
 
+// ---------------------------------------------------------------------------- direct moments
+// The slow path of the moment exchange: when a finalisation's wait for the other
+// tiles' moments runs out (or the host asks for it, see tria_score_wait_polls), the
+// workgroup scores every candidate slot of the group again, straight from the K
+// cache, and forms the group's moments itself: the result then never depends on the
+// other tiles' workgroups being resident.  The scores are the score kernel's own
+// (the same MFMA sequence per key); the moments are Welford updates per lane in fp64
+// merged in a fixed order, so they equal the exchanged ones up to rounding.
+
+// Scores of one 16-key block for every query head of the group, in the MFMA output
+// layout: after the hi + lo merge, lane (8 + h, grp) holds query head h's scores of
+// keys 4 grp .. 4 grp + 3 of the block (the same operation order as tile_body).
+template <int D, int P, bool MAXO>
+__device__ inline f32x4 block_scores(const ScoreArgs& a, size_t ug, const u32x4 (&ch)[D / 32],
+                                     const bf16x8 (&bdot)[D / 32], const bf16x8 (&bna)[D / 64],
+                                     const bf16x8 (&bnb)[D / 64], const u32x4 (&rref)[D / 64]) {
+  using S = Shape<D>;
+  const int lane = threadIdx.x & 63;
+  auto mag = [&](int q) {
+    const uint32_t w = rref[q / 8][(q % 8) / 2];
+    return __builtin_amdgcn_sqrtf(band_sq<D, P>(ch, q)) - ((q & 1) ? bf_hi(w) : bf_lo(w));
+  };
+  auto norm_part = [&](f32x4 acc) {
+#pragma unroll
+    for (int i = 0; i < S::NNC; ++i) {
+      u32x4 h4, l4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hi, lw;
+        split_bf16(mag(8 * i + 2 * j), mag(8 * i + 2 * j + 1), hi, lw);
+        h4[j] = hi;
+        l4[j] = lw;
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h4), bna[i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l4), bnb[i], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  f32x4 sc;
+  if constexpr (!MAXO) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < S::NKC; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[i]), bdot[i], acc, 0, 0, 0);
+    acc = norm_part(acc);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[t]), 0x118, 0xF, 0xF, true);
+      sc[t] = acc[t] + __int_as_float(other);
+    }
+  } else {
+    f32x4 best;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) best[t] = -__builtin_inff();
+    const u32x4* bm = reinterpret_cast<const u32x4*>(a.Bmax) + ug * a.ob.nblk * S::NKC * 64 + lane;
+    for (int cb = 0; cb < a.ob.nblk; ++cb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < S::NKC; ++i)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ch[i]),
+                                                      __builtin_bit_cast(bf16x8, bm[(cb * S::NKC + i) * 64]), acc,
+                                                      0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[t]), 0x118, 0xF, 0xF, true);
+        best[t] = __builtin_elementwise_maximum(best[t], acc[t] + __int_as_float(other));
+      }
+    }
+    for (int sft = a.ob.gp; sft < 8; sft *= 2) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int x = __float_as_int(best[t]);
+        const int y = sft == 1 ? __builtin_amdgcn_mov_dpp(x, 0x101, 0xF, 0xF, true)
+                    : sft == 2 ? __builtin_amdgcn_mov_dpp(x, 0x102, 0xF, 0xF, true)
+                               : __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);
+        best[t] = __builtin_elementwise_maximum(best[t], __int_as_float(y));
+      }
+    }
+    const f32x4 nrm = norm_part(f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int other = __builtin_amdgcn_mov_dpp(__float_as_int(nrm[t]), 0x118, 0xF, 0xF, true);
+      sc[t] = best[t] + nrm[t] + __int_as_float(other);
+    }
+  }
+  return sc;
+}
+
+// The moments (count, mean, M2) of every query head of group ug over its candidate
+// slots [sink, n - window), computed by the whole workgroup from the K cache; the
+// results go to s_mean / s_inv.  s_part: LDS scratch of kMaxGroup * 16 * 3 doubles.
+template <int D, int P, bool PAGED, bool MAXO>
+__device__ inline void group_moments_direct(const ScoreArgs& a, int ug, int n, double* s_part, float* s_mean,
+                                            float* s_inv) {
+  using S = Shape<D>;
+  constexpr int NB = S::NKC + 2 * S::NNC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int G = a.group;
+  const int u = ug / a.hkv, g = ug % a.hkv;
+  bf16x8 bdot[S::NKC], bna[S::NNC], bnb[S::NNC];
+  u32x4 rref[S::NR];
+  {
+    const u32x4* bsrc = reinterpret_cast<const u32x4*>(a.B) + (size_t)ug * S::NBT * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < S::NKC; ++i) bdot[i] = __builtin_bit_cast(bf16x8, bsrc[i * 64]);
+#pragma unroll
+    for (int i = 0; i < S::NNC; ++i) {
+      bna[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + i) * 64]);
+      bnb[i] = __builtin_bit_cast(bf16x8, bsrc[(S::NKC + S::NNC + i) * 64]);
+    }
+#pragma unroll
+    for (int i = 0; i < S::NR; ++i) rref[i] = bsrc[(NB + i) * 64];
+  }
+  const int c0 = min(a.sink, n), c1 = max(c0, n - a.window);
+  const bool owner = col >= 8 && col < 8 + G;
+  double cnt = 0.0, mean = 0.0, m2 = 0.0;      // Welford, per owner lane
+  for (int kb = c0 - c0 % 16 + 16 * wave; kb < c1; kb += 64) {
+    u32x4 ch[D / 32];
+    const int key = min(kb + col, n - 1);
+    const uint16_t* rp;
+    if (!PAGED) {
+      rp = a.k.base + (int64_t)u * a.k.su + (int64_t)g * a.k.sh + (int64_t)key * a.k.ss;
+    } else {
+      const int b0 = a.k.bt[(int64_t)u * a.k.mb + key / a.k.bs];
+      const int blk = b0 >= 0 && b0 < a.k.npb ? b0 : 0;
+      rp = a.k.base + ((int64_t)blk * a.k.bs + key % a.k.bs) * a.k.ss + (int64_t)g * a.k.sh;
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) ch[i] = *reinterpret_cast<const u32x4*>(rp + chunk_elem<D>(i, grp));
+    const f32x4 sc = block_scores<D, P, MAXO>(a, (size_t)ug, ch, bdot, bna, bnb, rref);
+    if (owner) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int k = kb + 4 * grp + t;
+        if (k >= c0 && k < c1) {
+          const double x = (double)sc[t];
+          cnt += 1.0;
+          const double d = x - mean;
+          mean += d / cnt;
+          m2 += d * (x - mean);
+        }
+      }
+    }
+  }
+  // partials [head][wave * 4 + grp], merged in that order
+  if (owner) {
+    double* q = s_part + ((col - 8) * 16 + wave * 4 + grp) * 3;
+    q[0] = cnt;
+    q[1] = mean;
+    q[2] = m2;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < G) {
+    const int h = threadIdx.x;
+    double c = 0.0, m = 0.0, mm = 0.0;
+    for (int i = 0; i < 16; ++i) chan_merge(c, m, mm, s_part[(h * 16 + i) * 3], s_part[(h * 16 + i) * 3 + 1],
+                                            s_part[(h * 16 + i) * 3 + 2]);
+    const double var = c > 0.0 ? fmax(mm / c, 0.0) : 0.0;
+    s_mean[h] = (float)(c > 0.0 ? m : 0.0);
+    s_inv[h] = (float)(1.0 / fmax(sqrt(var), 1e-12));
+  }
+  __syncthreads();
+}
+
 // Waits until every tile of the (unit, KV head) of `ti` has published its moments,
 // then z-normalises the tile's scores (still in LDS) per query head, aggregates the
 // GQA group onto the KV head [Fold note, sec. 4: normalize-then-max; mean is the
 // other variant] and writes the aggregate; protected slots (sinks, recent window)
 // get +inf.
+template <int D, int P, bool PAGED, bool MAXO>
 __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_known, const float* s_raw,
                                      uint32_t* s_hist) {
   const int lane = threadIdx.x & 63;
@@ -936,17 +1111,21 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
   const int hq = a.hkv * G;
   const int RS = a.tile + 16;
   __shared__ float s_mean[kMaxGroup], s_inv[kMaxGroup];
+  __shared__ int s_direct;   // a head's wait ran out: the group's moments are computed directly
   tile_len(a, ti, n_known >= 0 ? n_known : a.len[ti.u], false);
+  if (threadIdx.x == 0) s_direct = a.wait_polls < 0;
+  __syncthreads();
 
   // the group's mean and standard deviation per query head, from every tile's
   // (count, mean, M2) by the pairwise update of Chan, Golub and LeVeque (no
   // difference of large sums), in a fixed order: lane j merges tiles j, j + 64, ...
   // in turn, then a fixed shuffle tree merges the lanes.  A wave polls until none of
   // its head's moments reads kUnpublished.
-  for (int h = wave; h < G; h += 4) {
+  for (int h = wave; h < G && a.wait_polls >= 0; h += 4) {
     const unsigned long long* p =
         reinterpret_cast<const unsigned long long*>(a.part + ((size_t)ti.u * hq + ti.g * G + h) * a.n_tiles * 3);
     double c, m, m2;
+    bool expired = false;
     for (int polls = 0;; ++polls) {
       c = m = m2 = 0.0;
       bool missing = false;
@@ -958,11 +1137,15 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
         chan_merge(c, m, m2, __longlong_as_double(x0), __longlong_as_double(x1), __longlong_as_double(x2));
       }
       if (__ballot(missing) == 0) break;
-      if (polls >= kPollLimit) {
-        if (lane == 0) raise_flag(a.flags, kFlagSync);
+      if (polls >= a.wait_polls) {
+        expired = true;
         break;
       }
       __builtin_amdgcn_s_sleep(8);
+    }
+    if (expired) {
+      if (lane == 0) s_direct = 1;
+      continue;
     }
     for (int o = 32; o > 0; o >>= 1) {
       const double oc = __shfl_xor(c, o), om = __shfl_xor(m, o), om2 = __shfl_xor(m2, o);
@@ -973,6 +1156,12 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
       s_mean[h] = (float)(c > 0.0 ? m : 0.0);
       s_inv[h] = (float)(1.0 / fmax(sqrt(var), 1e-12));
     }
+  }
+  __syncthreads();
+  if (s_direct) {
+    // the histogram region is free until it is cleared below
+    if (threadIdx.x == 0) raise_flag(a.flags, kFlagSync);
+    group_moments_direct<D, P, PAGED, MAXO>(a, ti.ug, ti.n, reinterpret_cast<double*>(s_hist), s_mean, s_inv);
   }
   for (int i = threadIdx.x; i < kBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
@@ -1137,7 +1326,7 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
     // finalize uses the histogram region (for the maximum over offsets, the staged
     // offset blocks' region, restaged for the next tile)
     if (have_prev) {
-      finalize_tile(a, prev, known_len(prev), b ? buf0 : buf1, s_hist);
+      finalize_tile<D, P, PAGED, MAXO>(a, prev, known_len(prev), b ? buf0 : buf1, s_hist);
       if (MAXO && threadIdx.x == 0) s_bug = -1;
     }
     if (t >= total) break;

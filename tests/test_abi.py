@@ -293,3 +293,4 @@ def test_append_checks():
     assert _status(lambda: call(t=-1)) == L.TRIA_EINVAL
     assert _status(lambda: call(ws=None)) == L.TRIA_EWORKSPACE
     call(t=0)
+

@@ -471,3 +471,59 @@ def test_compaction_layout_paths_agree():
     torch.cuda.synchronize()
     for got, want in zip((prob.K_out, prob.V_out, prob.pos_out), ref):
         assert torch.equal(got, want)
+
+
+# ----------------------------------------------------------------------------- direct moments
+
+DIRECT = ["q8_small", "q32_small", "bd_small", "lc_small", "d256_neox", "d64_inter", "g7", "short_units",
+          "concentrated"]
+DIRECT_MAX = ["q8_max", "bd_max", "lc_max", "concentrated_max"]
+
+
+@pytest.mark.parametrize("name", DIRECT + DIRECT_MAX)
+def test_moments_computed_directly(name):
+    """With the moment exchange switched off (tria_score_wait_polls(-1)) every
+    finalisation computes its group's moments straight from the K cache: the path a
+    workgroup takes when its bounded wait runs out, so that results never depend on
+    the tiles' workgroups being resident together.  Checked against the oracle like
+    the small cases; TRIA_FLAG_SYNC records that the path ran."""
+    cfg = SMALL[name] if name in SMALL else MAXO[name]
+    prev = L.tria_score_wait_polls(-1)
+    try:
+        prob = _run(cfg)
+        flags = prob.flags()
+    finally:
+        L.tria_score_wait_polls(prev)
+    assert flags & L.FLAG_SYNC
+    assert flags & ~L.FLAG_SYNC == _expected_flags(cfg)
+    form = "direct" if cfg.offset_reduce == "max" else "folded"
+    kept = {unit: check_unit(prob, unit, form=form) for unit in range(cfg.n_units)}
+    _check_oracle_compaction(prob, kept)
+
+
+def test_direct_moments_schedule_independent():
+    """The direct path's moments run in a fixed order: aggregates, kept slots and
+    compacted rows are bit-identical for every cap on the persistent grid."""
+    cfg = SCHED["sched_g8"]
+    prev = L.tria_score_wait_polls(-1)
+    prev_cap = L.tria_score_max_workgroups(0)
+    try:
+        prob = _run(cfg)
+        ref = [t.clone() for t in (prob.agg, prob.idx, prob.cnt, prob.K_out, prob.V_out, prob.pos_out)]
+        n_tiles = -(-prob.n_max // 1024)
+        L.tria_score_max_workgroups(n_tiles)
+        for t in (prob.agg, prob.idx, prob.cnt, prob.K_out, prob.V_out, prob.pos_out):
+            t.zero_()
+        prob.run()
+        torch.cuda.synchronize()
+        assert prob.flags() & ~L.FLAG_SYNC == 0
+        u = synth.units(cfg)
+        for unit in range(cfg.n_units):
+            n = int(u.lengths[unit])
+            assert torch.equal(prob.agg[unit, :, :n], ref[0][unit, :, :n]), unit
+        for got, want in zip((prob.idx, prob.cnt, prob.K_out, prob.V_out, prob.pos_out), ref[1:]):
+            assert torch.equal(got, want)
+        check_unit(prob, 1)
+    finally:
+        L.tria_score_wait_polls(prev)
+        L.tria_score_max_workgroups(prev_cap)
