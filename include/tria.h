@@ -377,6 +377,28 @@ tria_status tria_stats_layer_budgets(int32_t n_units, const int32_t* unit_layer,
  * returns the previous cap. */
 int32_t tria_score_max_workgroups(int32_t cap);
 
+/* tria_pass_noalloc - the whole pass, tria_score (no per-query-head scores) ->
+ * tria_select -> tria_compact with the arguments of those three calls, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving loops
+ * or harnesses that forbid allocation): instead of a caller's workspace it uses a
+ * device array of the library's own, 96 MiB on each device the library runs on
+ * (held until the process ends; the largest workspace the five benchmark workloads
+ * need is 80 MiB).  It calls no allocating routine.  A pass whose workspace
+ * (tria_workspace_size) exceeds 96 MiB returns TRIA_EWORKSPACE.  Every check of the
+ * three calls runs before anything is launched.  The results equal those of the
+ * three calls.
+ *   flags  [device] int32, or NULL: receives this call's TRIA_FLAG_* word (the
+ *          array's flag word is cleared at the start of every call)
+ * All calls on one device share its array: calls that overlap in time on one device
+ * (other streams, other host threads) race and give unspecified results; order them
+ * on one stream. */
+tria_status tria_pass_noalloc(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t n_units,
+                              int32_t n_max, int32_t b_max, const int32_t* len, const int32_t* unit_layer,
+                              const int32_t* q_pos, const int32_t* budget, const float* q_mean_re,
+                              const float* q_mean_im, const float* q_abs_mean, const int32_t* pos_src,
+                              int32_t pos_heads, float* agg, int32_t* idx, int32_t* cnt, const tria_kv_view* k_dst,
+                              const tria_kv_view* v_dst, int32_t* pos_dst, int32_t* flags, void* stream);
+
 /* Polls of tria_score's bounded wait for a group's tile moments (the default,
  * 65536, is ~0.1-0.2 s).  When a wait runs out, the workgroup computes the group's
  * moments directly from the K cache instead (TRIA_FLAG_SYNC is raised as

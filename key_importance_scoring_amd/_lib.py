@@ -28,7 +28,7 @@ EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "
            "tria_score_max_workgroups", "tria_score_wait_polls", "tria_select_strategy",
            "tria_calibrate_workspace_size",
            "tria_calibrate", "tria_compact_inplace", "tria_append", "tria_stats_parse", "tria_stats_encode",
-           "tria_stats_band_mask", "tria_stats_layer_budgets")
+           "tria_stats_band_mask", "tria_stats_layer_budgets", "tria_pass_noalloc")
 
 
 class TriaError(RuntimeError):
@@ -117,6 +117,11 @@ def load() -> ctypes.CDLL:
     lib.tria_append.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_void_p, c_int32,
                                 c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p]
+    lib.tria_pass_noalloc.restype = c_int32
+    lib.tria_pass_noalloc.argtypes = [POINTER(TriaParams), POINTER(TriaKvView), POINTER(TriaKvView), c_int32, c_int32,
+                                      c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_int32, c_void_p, c_void_p, c_void_p, POINTER(TriaKvView),
+                                      POINTER(TriaKvView), c_void_p, c_void_p, c_void_p]
     lib.tria_stats_parse.restype = c_int32
     lib.tria_stats_parse.argtypes = [c_void_p, c_size_t, POINTER(TriaStatsInfo), c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p]
@@ -222,6 +227,16 @@ def tria_append(p: TriaParams, k: TriaKvView, v: TriaKvView, pos, n_units: int, 
     _check(load().tria_append(ctypes.byref(p), ctypes.byref(k), ctypes.byref(v), ptr(pos), n_units, n_max, ptr(len_),
                               ptr(q_pos), t_new, ptr(k_new), ptr(v_new), ptr(pos_new), ptr(ws),
                               stream_handle(stream)))
+
+
+def tria_pass_noalloc(p: TriaParams, k: TriaKvView, v: TriaKvView, n_units: int, n_max: int, b_max: int, len_,
+                      unit_layer, q_pos, budget, q_mean_re, q_mean_im, q_abs_mean, pos_src, pos_heads: int, agg, idx,
+                      cnt, k_dst: TriaKvView, v_dst: TriaKvView, pos_dst, flags=None, stream=None) -> None:
+    _check(load().tria_pass_noalloc(ctypes.byref(p), ctypes.byref(k), ctypes.byref(v), n_units, n_max, b_max,
+                                    ptr(len_), ptr(unit_layer), ptr(q_pos), ptr(budget), ptr(q_mean_re),
+                                    ptr(q_mean_im), ptr(q_abs_mean), ptr(pos_src), pos_heads, ptr(agg), ptr(idx),
+                                    ptr(cnt), ctypes.byref(k_dst), ctypes.byref(v_dst), ptr(pos_dst), ptr(flags),
+                                    stream_handle(stream)))
 
 
 def tria_device_flags(ws, stream=None) -> int:

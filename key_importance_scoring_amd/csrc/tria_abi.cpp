@@ -45,7 +45,8 @@ struct Rec {
 std::mutex g_tmu;
 bool g_timing = false;
 std::vector<Rec> g_recs;
-
+// set while tria_pass_noalloc runs on this thread: no timing events are created
+thread_local bool t_no_events = false;
 
 // Runs `launch` on `stream`, bracketed by HIP events on the same stream when
 // timing is on.  The events skip the system-scope fence (an L2 writeback and
@@ -56,7 +57,7 @@ hipError_t timed(int id, hipStream_t stream, Fn&& launch) {
   bool on;
   {
     std::lock_guard<std::mutex> lk(g_tmu);
-    on = g_timing;
+    on = g_timing && !t_no_events;
   }
   if (!on) return launch();
   Rec r{id, nullptr, nullptr};
@@ -469,6 +470,47 @@ tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_
                       static_cast<int32_t*>(ws)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launch_status(tria::launch_append(aa, s), "k_append");
+}
+
+tria_status tria_pass_noalloc(const tria_params* p, const tria_kv_view* k, const tria_kv_view* v, int32_t n_units,
+                              int32_t n_max, int32_t b_max, const int32_t* len, const int32_t* unit_layer,
+                              const int32_t* q_pos, const int32_t* budget, const float* q_mean_re,
+                              const float* q_mean_im, const float* q_abs_mean, const int32_t* pos_src,
+                              int32_t pos_heads, float* agg, int32_t* idx, int32_t* cnt, const tria_kv_view* k_dst,
+                              const tria_kv_view* v_dst, int32_t* pos_dst, int32_t* flags, void* stream) {
+  tria_status st = check_params(p);
+  if (st != TRIA_OK) return st;
+  if (n_units < 0 || n_max < 0 || b_max < 0) return fail(TRIA_EINVAL, "n_units, n_max and b_max must be >= 0");
+  const size_t need = layout(p, n_units, n_max).total;
+  if (need > tria::kScratchBytes)
+    return fail(TRIA_EWORKSPACE, "the pass needs %zu bytes of workspace; the library's scratch holds %zu", need,
+                tria::kScratchBytes);
+  hipError_t e = hipSuccess;
+  void* ws = tria::scratch_address(&e);
+  if (!ws) return fail(TRIA_ELAUNCH, "scratch address: %s", hipGetErrorString(e));
+  const size_t wsb = tria::kScratchBytes;
+  // every step's checks before anything is launched
+  if ((st = score_impl(p, k, n_units, n_max, len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, nullptr, agg,
+                       ws, wsb, stream, true)) != TRIA_OK ||
+      (st = select_impl(p, n_units, n_max, b_max, len, budget, agg, idx, cnt, ws, wsb, stream, true)) != TRIA_OK ||
+      (st = compact_impl(p, k, v, pos_src, pos_heads, n_units, n_max, b_max, len, idx, cnt, k_dst, v_dst, pos_dst,
+                         stream, true)) != TRIA_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  struct NoEvents {
+    NoEvents() { t_no_events = true; }
+    ~NoEvents() { t_no_events = false; }
+  } no_events;
+  // the flag word starts at zero for every call (the scratch keeps the last call's contents)
+  if ((st = launch_status(tria::launch_set_word(static_cast<int32_t*>(ws), 0, s), "flag word")) != TRIA_OK) return st;
+  if ((st = score_impl(p, k, n_units, n_max, len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, nullptr, agg,
+                       ws, wsb, stream, false)) != TRIA_OK ||
+      (st = select_impl(p, n_units, n_max, b_max, len, budget, agg, idx, cnt, ws, wsb, stream, false)) != TRIA_OK ||
+      (st = compact_impl(p, k, v, pos_src, pos_heads, n_units, n_max, b_max, len, idx, cnt, k_dst, v_dst, pos_dst,
+                         stream, false)) != TRIA_OK)
+    return st;
+  if (flags) st = launch_status(tria::launch_copy_word(flags, static_cast<const int32_t*>(ws), s), "flag word");
+  return st;
 }
 
 tria_status tria_device_flags(void* ws, int32_t* flags, void* stream) {

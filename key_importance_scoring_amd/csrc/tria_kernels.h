@@ -246,5 +246,15 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+// The no-allocation pass's workspace: a file-scope device array of this many bytes
+// in tria_kernels.hip (every benchmark workload's workspace fits; the largest, 64
+// layers x 8 KV heads x 32768 slots, needs 80 MiB).
+constexpr size_t kScratchBytes = size_t(96) << 20;
+// Its device address on the current device (looked up once per device), or null
+// with *err set.
+void* scratch_address(hipError_t* err);
+// One-thread kernels: *dst = v, *dst = *src (flag word handling without memset or copies).
+hipError_t launch_set_word(int32_t* dst, int32_t v, hipStream_t s);
+hipError_t launch_copy_word(int32_t* dst, const int32_t* src, hipStream_t s);
 
 }  // namespace tria

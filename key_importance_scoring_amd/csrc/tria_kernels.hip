@@ -35,6 +35,7 @@
 #include "tria_kernels.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace tria {
@@ -2404,6 +2405,50 @@ hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_set_len, dim3((unsigned)((a.n_units + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ============================================================================ no-allocation pass
+// The workspace of tria_pass_noalloc: a device array of the library's own, so that
+// callers that cannot allocate device memory can run the pass.  Each device holds
+// its own copy at its own address, found once per device with hipGetSymbolAddress;
+// host code passes only that address to kernels (the array's name in host code is
+// not a device address).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* scratch_address(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+namespace {
+__global__ void k_set_word(int32_t* dst, int32_t v) { *dst = v; }
+__global__ void k_copy_word(int32_t* dst, const int32_t* src) { *dst = *src; }
+}  // namespace
+
+hipError_t launch_set_word(int32_t* dst, int32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_word, dim3(1), dim3(1), 0, s, dst, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_word(int32_t* dst, const int32_t* src, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(1), 0, s, dst, src);
   return hipGetLastError();
 }
 

@@ -294,3 +294,22 @@ def test_append_checks():
     assert _status(lambda: call(ws=None)) == L.TRIA_EWORKSPACE
     call(t=0)
 
+
+def test_pass_noalloc_checks():
+    """The allocation-free pass rejects a workspace beyond its 96 MiB array, and bad
+    parameters, before any HIP call."""
+    p = _params()
+    k = _view()
+    v = _view(A + 2 * 8 * 4096 * 128 * 2)
+    kd = _view(A + 4 * 8 * 4096 * 128 * 2)
+    vd = _view(A + 6 * 8 * 4096 * 128 * 2)
+
+    def call(p=p, n_units=2, n_max=4096):
+        L.tria_pass_noalloc(p, k, v, n_units, n_max, 2048, A, A, A, A, A, A, A, A, 1, A, A, A, kd, vd, A)
+
+    assert _status(lambda: call(p=_params(pairing=5))) == L.TRIA_EINVAL
+    assert _status(lambda: call(n_units=-1)) == L.TRIA_EINVAL
+    # 300 units x 8 KV heads x 32768 slots need far more than 96 MiB of workspace
+    assert L.tria_workspace_size(p, 300, 32768) > 96 << 20
+    assert _status(lambda: call(n_units=300, n_max=32768)) == L.TRIA_EWORKSPACE
+    assert "scratch holds" in L.load().tria_last_error().decode()
