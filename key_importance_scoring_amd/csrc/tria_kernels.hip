@@ -501,7 +501,9 @@ __device__ inline void load_stage(Stage<D, MAXO>& ch, const KView& k, int u, int
       rp = k.base + ((int64_t)blk * k.bs + key % k.bs) * k.ss + (int64_t)g * k.sh;
     }
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) ch[b][i] = *reinterpret_cast<const u32x4*>(rp + chunk_elem<D>(i, grp));
+    for (int i = 0; i < D / 32; ++i) {
+      ch[b][i] = *reinterpret_cast<const u32x4*>(rp + chunk_elem<D>(i, grp));
+    }
   }
 }
 
@@ -1840,9 +1842,11 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
     uint16_t* kd = const_cast<uint16_t*>(row_ptr(a.kd, u, g, j, a.flags));
     uint16_t* vd = const_cast<uint16_t*>(row_ptr(a.vd, u, g, j, a.flags));
     if (ks && kd)
-      reinterpret_cast<u32x4*>(kd)[part] = reinterpret_cast<const u32x4*>(ks)[part];
+      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks) + part),
+                                  reinterpret_cast<u32x4*>(kd) + part);
     if (vs && vd)
-      reinterpret_cast<u32x4*>(vd)[part] = reinterpret_cast<const u32x4*>(vs)[part];
+      __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs) + part),
+                                  reinterpret_cast<u32x4*>(vd) + part);
     if (part == 0 && a.pos_src && a.pos_dst) {
       const int ph = a.pos_heads > 1 ? g : 0;
       a.pos_dst[((size_t)u * a.hkv + g) * a.b_max + j] =
@@ -1859,7 +1863,9 @@ __global__ __launch_bounds__(256) void k_compact(CompactArgs a) {
 // the indices (and destination block ids), one for the source block ids and
 // positions (paged sources), and one for the rows.  Every load is unconditional:
 // rows past the count and invalid slots or block ids read a clamped, existing
-// address and are not stored.
+// address and are not stored.  The rows are loaded and stored non-temporally (both
+// compaction kernels): they are touched once, and dirty lines left in the caches would
+// otherwise be written back while the next pass's score kernel streams the cache.
 template <int D, bool SP, bool DP>
 __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a) {
   constexpr int LPR = D / 8;                // lanes per row, 16 bytes each
@@ -1918,8 +1924,8 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a) {
       ko = (int64_t)u * a.ks.su + (int64_t)g * a.ks.sh + (int64_t)slot[k] * a.ks.ss;
       vo = (int64_t)u * a.vs.su + (int64_t)g * a.vs.sh + (int64_t)slot[k] * a.vs.ss;
     }
-    kv[k] = reinterpret_cast<const u32x4*>(a.ks.base + ko)[part];
-    vv[k] = reinterpret_cast<const u32x4*>(a.vs.base + vo)[part];
+    kv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.ks.base + ko) + part);
+    vv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vs.base + vo) + part);
   }
   // step 4: stores
 #pragma unroll
@@ -1938,8 +1944,8 @@ __global__ __launch_bounds__(256) void k_compact_fast(CompactArgs a) {
       vo = (int64_t)u * a.vd.su + (int64_t)g * a.vd.sh + (int64_t)j * a.vd.ss;
     }
     if (okd) {
-      reinterpret_cast<u32x4*>(a.kd.base + ko)[part] = kv[k];
-      reinterpret_cast<u32x4*>(a.vd.base + vo)[part] = vv[k];
+      __builtin_nontemporal_store(kv[k], reinterpret_cast<u32x4*>(a.kd.base + ko) + part);
+      __builtin_nontemporal_store(vv[k], reinterpret_cast<u32x4*>(a.vd.base + vo) + part);
       if (part == 0 && a.pos_src && a.pos_dst) a.pos_dst[(size_t)ug * a.b_max + j] = pos[k];
     }
   }
