@@ -153,7 +153,7 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 
 // ------------------------------------------------------------------ workspace
 struct Layout {
-  size_t B, Bmax, nconst, part, claim, hist, st, tiles, list, masks, total;
+  size_t B, Bmax, nconst, part, gstat, arrive, claim, hist, st, tiles, list, masks, total;
   int32_t tile, n_tiles, n_st;   // keys per score tile, score tiles and selection tiles per row
   tria::OffsetBlocks ob;
 };
@@ -161,9 +161,9 @@ struct Layout {
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace: [flag word | MFMA B operands and reference magnitudes | (maximum over
-// offsets) offset-block B operands | norm constants | tile moments | tile claim
-// counter | aggregate histograms | selection state | per-tile counts | candidates |
-// per-tile slot masks]
+// offsets) offset-block B operands | norm constants | tile moments | merged moments |
+// tile arrival counts | tile claim counter | aggregate histograms | selection state |
+// per-tile counts | candidates | per-tile slot masks]
 Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   Layout L{};
   const size_t U = (size_t)n_units, hq = (size_t)p->n_kv_heads * p->group, d = (size_t)p->head_dim;
@@ -180,6 +180,10 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   off += al256(U * hq * 4);
   L.part = off;
   off += al256(U * hq * (size_t)L.n_tiles * 3 * 8);
+  L.gstat = off;
+  off += al256(U * hq * 8);
+  L.arrive = off;
+  off += al256(U * (size_t)p->n_kv_heads * 4);
   L.claim = off;
   off += 256;  // the tile claim counter
   L.hist = off;
@@ -268,14 +272,16 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
                     p->pairing, std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean,
                     p->group, L.n_tiles, L.tile, n_max, B, nconst,
                     reinterpret_cast<uint64_t*>(part), next_tile, hist, flags, omax,
-                    reinterpret_cast<uint32_t*>(w + L.Bmax), L.ob};
+                    reinterpret_cast<uint32_t*>(w + L.Bmax), L.ob, reinterpret_cast<uint64_t*>(w + L.gstat),
+                    reinterpret_cast<int32_t*>(w + L.arrive)};
   hipError_t e = timed(kIdCoef, s, [&] { return tria::launch_coef(ca, offs, s); });
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
                      L.tile, L.n_tiles, p->agg,
                      len, B, nconst, raw, part, agg, next_tile, hist, flags, omax,
-                     reinterpret_cast<const uint32_t*>(w + L.Bmax), L.ob, g_wait_polls.load()};
+                     reinterpret_cast<const uint32_t*>(w + L.Bmax), L.ob, g_wait_polls.load(),
+                     reinterpret_cast<uint64_t*>(w + L.gstat), reinterpret_cast<int32_t*>(w + L.arrive)};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, wg_cap, s); });
   return launch_status(e, "k_score");
 }

@@ -40,9 +40,13 @@ constexpr uint64_t kUnpublished = ~0ull;
 // short sleep (~0.1-0.2 s in all); when it runs out the group's moments are computed
 // directly from the K cache.
 constexpr int kPollLimit = 1 << 16;
-// Linear bins of an aggregate (a z-score: scale-free): 2048 bins over [-8, 8), one
-// below, one above, one for +inf (protected slots).
-constexpr int kBins = 2052;
+// Linear bins of an aggregate (a z-score: scale-free): kBinScale bins per unit over
+// [-8, 8), one below, one above, one for +inf (protected slots), one spare.
+#ifndef TRIA_BIN_SCALE
+#define TRIA_BIN_SCALE 64
+#endif
+constexpr int kBinScale = TRIA_BIN_SCALE;
+constexpr int kBins = 16 * kBinScale + 4;
 
 // Coefficient blocks of the maximum-over-offsets mode (16 MFMA B columns each:
 // hi parts in columns 0..7, lo parts in 8..15).  With G' = G rounded up to a power
@@ -110,6 +114,8 @@ struct CoefArgs {
   int32_t omax;               // 1: maximum over the offsets
   uint32_t* Bmax;             // omax: [U][Hkv][nblk][d/32][64] 16-byte B operands of the offset blocks
   OffsetBlocks ob;
+  uint64_t* gstat;            // [U][Hq] each query head's merged (mean, 1 / deviation), set to kUnpublished here
+  int32_t* arrive;            // [U][Hkv] scored tiles counted in, cleared here
 };
 
 struct ScoreArgs {
@@ -128,6 +134,8 @@ struct ScoreArgs {
   const uint32_t* Bmax;       // omax: [U][Hkv][nblk][d/32][64] 16-byte B operands of the offset blocks
   OffsetBlocks ob;
   int32_t wait_polls;         // polls of a finalisation's wait (< 0: compute the moments directly at once)
+  uint64_t* gstat;            // [U][Hq] merged (mean, 1 / deviation) per query head: two fp32 in one word
+  int32_t* arrive;            // [U][Hkv] non-empty tiles that have published their moments
 };
 
 // Per-(unit, KV head) state of the selection, in the workspace.

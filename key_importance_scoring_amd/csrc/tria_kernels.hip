@@ -88,7 +88,7 @@ __device__ inline int lin_bin(float x) {
   if (x == __builtin_inff()) return kBins - 1;
   if (x >= 8.0f) return kBins - 2;
   if (x < -8.0f) return 0;
-  return 1 + (int)((x + 8.0f) * 128.0f);  // [1, 2048]
+  return 1 + (int)((x + 8.0f) * (float)kBinScale);  // [1, 16 kBinScale + 1]
 }
 
 template <class V>
@@ -153,7 +153,8 @@ __device__ inline int lane_band(int q, int c) {
 // once per band; each (query head, band) of the group then forms its coefficient
 // into LDS, and the block finally writes them as k_score's MFMA B operands, in the
 // order its lanes load them (the MFMA operand layout above).  The block also
-// resets its (unit, KV head)'s tile moments to kUnpublished and clears its
+// resets its (unit, KV head)'s tile moments and merged moments to kUnpublished and
+// its tile arrival count to 0, and clears its
 // aggregate histogram; block (0, 0) clears the tile claim counter.
 // sin and cos of an fp64 angle: reduced modulo 2 pi in fp64, then the fp32 sine and
 // cosine of the remainder (|error| ~1e-7, far below the ~2^-17 relative precision of
@@ -224,6 +225,8 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
       a.part[ug * per + i] = (int64_t)tile * a.tile >= n_u ? 0ull : kUnpublished;
     }
     for (int i = t; i < kBins; i += 256) a.hist[ug * kBins + i] = 0u;
+    if (t < G) a.gstat[ug * G + t] = kUnpublished;
+    if (t == 0) a.arrive[ug] = 0;
     if (u == 0 && g == 0 && t == 0) *a.next_tile = 0;
   }
 
@@ -833,6 +836,60 @@ __device__ inline void tile_body(const ScoreArgs& a, TileInfo& ti, float* s_raw,
   __syncthreads();
 }
 
+// Adds the moments (nb, mb, M2b) of a set of scores to the running (n, m, M2):
+// count, mean and sum of squared deviations of the union (the pairwise update of
+// Chan, Golub and LeVeque).  An empty set (nb = 0) changes nothing; an empty running
+// set takes the other's moments as they are.
+__device__ inline void chan_merge(double& n, double& m, double& M2, double nb, double mb, double M2b) {
+  const double nt = n + nb;
+  if (nt > 0.0) {
+    const double d = mb - m;
+    const double f = nb / nt;
+    m += d * f;
+    M2 += M2b + d * d * n * f;
+  }
+  n = nt;
+}
+
+// One query head's moments over every tile of its (unit, KV head), from each tile's
+// (count, mean, M2) by the pairwise update of Chan, Golub and LeVeque (no difference
+// of large sums), in a fixed order: lane j merges tiles j, j + 64, ... in turn, then
+// a fixed shuffle tree merges the lanes.  One wave; polls until none of the head's
+// moments reads kUnpublished, at most a.wait_polls times.  Returns false when the
+// wait ran out; else every lane holds the group's count c, mean m and M2.
+__device__ inline bool merge_head(const ScoreArgs& a, size_t qh, double& c, double& m, double& m2) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long* p = reinterpret_cast<const unsigned long long*>(a.part + qh * a.n_tiles * 3);
+  for (int polls = 0;; ++polls) {
+    c = m = m2 = 0.0;
+    bool missing = false;
+    for (int j = lane; j < a.n_tiles; j += 64) {
+      const unsigned long long x0 = __hip_atomic_load(p + 3 * j + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long x1 = __hip_atomic_load(p + 3 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long x2 = __hip_atomic_load(p + 3 * j + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      missing |= (x0 == kUnpublished) | (x1 == kUnpublished) | (x2 == kUnpublished);
+      chan_merge(c, m, m2, __longlong_as_double(x0), __longlong_as_double(x1), __longlong_as_double(x2));
+    }
+    if (__ballot(missing) == 0) break;
+    if (polls >= a.wait_polls) return false;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const double oc = __shfl_xor(c, o), om = __shfl_xor(m, o), om2 = __shfl_xor(m2, o);
+    chan_merge(c, m, m2, oc, om, om2);
+  }
+  return true;
+}
+
+// The group's mean and inverse standard deviation of one query head from its merged
+// moments, as two fp32 in one word (mean in the low half).
+__device__ inline uint64_t pack_stats(double c, double m, double m2) {
+  const double var = c > 0.0 ? fmax(m2 / c, 0.0) : 0.0;
+  const float mean = (float)(c > 0.0 ? m : 0.0);
+  const float inv = (float)(1.0 / fmax(sqrt(var), 1e-12));
+  return (uint64_t)__float_as_uint(mean) | ((uint64_t)__float_as_uint(inv) << 32);
+}
+
 // The end of a scored tile (lengths filled by tile_body): its per-query-head scores
 // (if wanted) and its candidate moments (count, mean, sum of squared deviations),
 // published for the other tiles of its (unit, KV head).
@@ -918,21 +975,29 @@ __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const fl
   }
   // nothing waits for these stores: each moment is a single-copy-atomic 8-byte
   // store, and a reader takes it as published once it no longer reads kUnpublished
-}
 
-// Adds the moments (nb, mb, M2b) of a set of scores to the running (n, m, M2):
-// count, mean and sum of squared deviations of the union (the pairwise update of
-// Chan, Golub and LeVeque).  An empty set (nb = 0) changes nothing; an empty running
-// set takes the other's moments as they are.
-__device__ inline void chan_merge(double& n, double& m, double& M2, double nb, double mb, double M2b) {
-  const double nt = n + nb;
-  if (nt > 0.0) {
-    const double d = mb - m;
-    const double f = nb / nt;
-    m += d * f;
-    M2 += M2b + d * d * n * f;
+  // The last non-empty tile of the (unit, KV head) to count itself in merges every
+  // tile's moments once (instead of once per finalisation) and publishes each query
+  // head's mean and inverse deviation; the others' moments are already issued, so its
+  // wait is short.  If that wait runs out, nothing is published and the finalisations
+  // compute the moments directly.
+  if (tlen > 0 && a.wait_polls >= 0) {
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(a.arrive + ti.ug, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+               (n + a.tile - 1) / a.tile;
+    __syncthreads();
+    if (s_last) {
+      for (int h = wave; h < G; h += 4) {
+        double c, m, m2;
+        const size_t qh = (size_t)u * hq + g * G + h;
+        if (merge_head(a, qh, c, m, m2) && lane == 0)
+          __hip_atomic_store(a.gstat + qh, (unsigned long long)pack_stats(c, m, m2), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
-  n = nt;
 }
 
 // ---------------------------------------------------------------------------- direct moments
@@ -1026,6 +1091,9 @@ __device__ inline f32x4 block_scores(const ScoreArgs& a, size_t ug, const u32x4 
 // The moments (count, mean, M2) of every query head of group ug over its candidate
 // slots [sink, n - window), computed by the whole workgroup from the K cache; the
 // results go to s_mean / s_inv.  s_part: LDS scratch of kMaxGroup * 16 * 3 doubles.
+// finalize_tile lends the histogram region (kBins words) to group_moments_direct
+static_assert(kBins >= kMaxGroup * 16 * 3 * 2, "the histogram region holds the direct moments' scratch");
+
 template <int D, int P, bool PAGED, bool MAXO>
 __device__ inline void group_moments_direct(const ScoreArgs& a, int ug, int n, double* s_part, float* s_mean,
                                             float* s_inv) {
@@ -1100,8 +1168,8 @@ __device__ inline void group_moments_direct(const ScoreArgs& a, int ug, int n, d
   __syncthreads();
 }
 
-// Waits until every tile of the (unit, KV head) of `ti` has published its moments,
-// then z-normalises the tile's scores (still in LDS) per query head, aggregates the
+// Waits until the group's last tile has published the merged moments of the (unit,
+// KV head) of `ti` (tile_end), then z-normalises the tile's scores (still in LDS) per query head, aggregates the
 // GQA group onto the KV head [Fold note, sec. 4: normalize-then-max; mean is the
 // other variant] and writes the aggregate; protected slots (sinks, recent window)
 // get +inf.
@@ -1119,45 +1187,27 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
   if (threadIdx.x == 0) s_direct = a.wait_polls < 0;
   __syncthreads();
 
-  // the group's mean and standard deviation per query head, from every tile's
-  // (count, mean, M2) by the pairwise update of Chan, Golub and LeVeque (no
-  // difference of large sums), in a fixed order: lane j merges tiles j, j + 64, ...
-  // in turn, then a fixed shuffle tree merges the lanes.  A wave polls until none of
-  // its head's moments reads kUnpublished.
-  for (int h = wave; h < G && a.wait_polls >= 0; h += 4) {
+  // the group's mean and inverse standard deviation per query head, merged once by
+  // the group's last tile (tile_end): wave 0 polls the G words until none reads
+  // kUnpublished, at most a.wait_polls times
+  if (wave == 0 && a.wait_polls >= 0) {
     const unsigned long long* p =
-        reinterpret_cast<const unsigned long long*>(a.part + ((size_t)ti.u * hq + ti.g * G + h) * a.n_tiles * 3);
-    double c, m, m2;
-    bool expired = false;
+        reinterpret_cast<const unsigned long long*>(a.gstat + (size_t)ti.u * hq + ti.g * G);
     for (int polls = 0;; ++polls) {
-      c = m = m2 = 0.0;
-      bool missing = false;
-      for (int j = lane; j < a.n_tiles; j += 64) {
-        const unsigned long long x0 = __hip_atomic_load(p + 3 * j + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long x1 = __hip_atomic_load(p + 3 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long x2 = __hip_atomic_load(p + 3 * j + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        missing |= (x0 == kUnpublished) | (x1 == kUnpublished) | (x2 == kUnpublished);
-        chan_merge(c, m, m2, __longlong_as_double(x0), __longlong_as_double(x1), __longlong_as_double(x2));
+      const unsigned long long w =
+          lane < G ? __hip_atomic_load(p + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      if (__ballot(w == kUnpublished) == 0) {
+        if (lane < G) {
+          s_mean[lane] = __uint_as_float((uint32_t)w);
+          s_inv[lane] = __uint_as_float((uint32_t)(w >> 32));
+        }
+        break;
       }
-      if (__ballot(missing) == 0) break;
       if (polls >= a.wait_polls) {
-        expired = true;
+        if (lane == 0) s_direct = 1;
         break;
       }
       __builtin_amdgcn_s_sleep(8);
-    }
-    if (expired) {
-      if (lane == 0) s_direct = 1;
-      continue;
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      const double oc = __shfl_xor(c, o), om = __shfl_xor(m, o), om2 = __shfl_xor(m2, o);
-      chan_merge(c, m, m2, oc, om, om2);
-    }
-    if (lane == 0) {
-      const double var = c > 0.0 ? fmax(m2 / c, 0.0) : 0.0;
-      s_mean[h] = (float)(c > 0.0 ? m : 0.0);
-      s_inv[h] = (float)(1.0 / fmax(sqrt(var), 1e-12));
     }
   }
   __syncthreads();
@@ -1353,15 +1403,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // ============================================================================ selection
 // tria_select keeps, per (unit, KV head), the K = min(B, n) slots with the largest
-// aggregates (ties to the lower slot), in four steps; the two tile-parallel steps
-// carry all the per-slot work, the per-group steps touch only histograms, a short
-// candidate list and per-tile counts:
-//   k_sel_thresh  (per group) the histogram of the aggregates' linear bins, built by
-//                 k_score, gives the bin b1 holding the K-th largest; the binning is
-//                 monotone, so every slot in a higher bin is kept and every slot in a
-//                 lower bin dropped;
-//   k_sel_collect (per tile)  counts the tile's slots above b1 and lists its slots of
-//                 b1 in the tile's own segment of the group's candidate list;
+// aggregates (ties to the lower slot), in three steps; the two tile-parallel steps
+// carry all the per-slot work, the per-group step touches only a short candidate
+// list and per-tile counts:
+//   k_sel_collect (per tile)  wave 0 finds, in the histogram of the aggregates'
+//                 linear bins that k_score built, the bin b1 holding the K-th
+//                 largest (the binning is monotone, so every slot in a higher bin is
+//                 kept and every slot in a lower bin dropped) while the tile's
+//                 aggregates load; then the tile counts its slots above b1 and lists
+//                 its slots of b1 in its own segment of the group's candidate list;
 //   k_sel_refine  (per group) exact radix passes (11 + 11 + 10 bits of the
 //                 order-preserving key) over the candidates give the threshold key T
 //                 and how many slots equal to T are kept (the lowest ones); then each
@@ -1404,56 +1454,103 @@ __device__ inline void find_digit(const uint32_t* hist, int nb, uint32_t krem, u
 
 // The selection's bounds for group ug: n cached slots, K kept, and the bin b1
 // holding the K-th largest aggregate (-1: keep everything; kBins: keep nothing) with
-// krem slots still to take from it; flags and cnt[u] are written here.
-__global__ __launch_bounds__(256) void k_sel_thresh(SelectArgs a) {
-  constexpr int NT = 256;
-  const int ug = blockIdx.x;
-  const int u = ug / a.hkv, g = ug % a.hkv;
-  const bool lead = g == 0 && threadIdx.x == 0;
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wtot[4];
-  __shared__ uint32_t sh[2];
-  struct {
-    int n, K, b1;
-    uint32_t krem;
-  } r;
-  r.n = clamp_len(a.len, u, a.n_max, lead ? a.flags : nullptr);
+// krem slots still to take from it.  Formed by one wave (every lane returns the same
+// values): lane l holds the kSelPL consecutive bins from kSelPL l, an inclusive scan
+// from the top lane down gives each lane the count in its bins and above, the lane
+// where that count first reaches K walks its own bins from the top.  A histogram
+// holding fewer than K slots (len changed since tria_score, outside the contract)
+// gives b1 = -1: the first K slots are kept.  `lead` raises the group's flags.
+constexpr int kSelPL = (kBins + 63) / 64;
+struct SelBounds {
+  int n, K, b1;
+  uint32_t krem;
+};
+
+__device__ inline SelBounds sel_bounds(const SelectArgs& a, int ug, int u, bool lead) {
+  const int lane = threadIdx.x & 63;
+  uint32_t h[kSelPL];
+  {
+    const uint32_t* gh = a.hist + (size_t)ug * kBins + kSelPL * lane;
+#pragma unroll
+    for (int i = 0; i < kSelPL; ++i) h[i] = kSelPL * lane + i < kBins ? gh[i] : 0u;
+  }
+  int32_t* flags = lead && lane == 0 ? a.flags : nullptr;
+  SelBounds r;
+  r.n = clamp_len(a.len, u, a.n_max, flags);
   int B = a.budget[u];
   const int prot = min(r.n, a.sink + a.window);
   if (B < 0 || (r.n > B && B < prot)) {
-    if (lead) raise_flag(a.flags, kFlagBudget);
+    if (flags) raise_flag(flags, kFlagBudget);
     B = B < 0 ? 0 : B;
   }
   r.K = B < r.n ? B : r.n;
   if (r.K > a.b_max) {
-    if (lead) raise_flag(a.flags, kFlagBmax);
+    if (flags) raise_flag(flags, kFlagBmax);
     r.K = a.b_max;
   }
-  if (lead) a.cnt[u] = r.K;
   r.krem = 0;
   if (r.K == 0) {
     r.b1 = kBins;
   } else if (r.K >= r.n) {
     r.b1 = -1;
   } else {
-    const uint32_t* gh = a.hist + (size_t)ug * kBins;
-    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = gh[i];
-    __syncthreads();
-    uint32_t d, above;
-    find_digit<NT>(hist, kBins, (uint32_t)r.K, wtot, sh, d, above);
-    r.b1 = (int)d;
-    r.krem = (uint32_t)r.K - above;
+    const uint32_t K = (uint32_t)r.K;
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPL; ++i) local += h[i];
+    uint32_t incl = local;   // slots in the bins of this lane and every lane above it
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_down(incl, o);
+      if (lane + o < 64) incl += v;
+    }
+    const uint32_t excl = incl - local;
+    const bool mine = excl < K && K <= incl;
+    int bin = 0;
+    uint32_t above = 0, acc = excl;
+    bool done = false;
+#pragma unroll
+    for (int i = kSelPL - 1; i >= 0; --i) {
+      const bool hit = mine && !done && acc + h[i] >= K;
+      if (hit) {
+        bin = kSelPL * lane + i;
+        above = acc;
+      }
+      done |= hit;
+      acc += h[i];
+    }
+    const unsigned long long m = __ballot(mine);
+    if (m == 0) {
+      r.b1 = -1;
+    } else {
+      const int src = __ffsll((long long)m) - 1;
+      r.b1 = __shfl(bin, src);
+      r.krem = K - (uint32_t)__shfl((int)above, src);
+    }
   }
-  if (threadIdx.x == 0) {
-    SelState& st = a.st[ug];
-    st.b1 = r.b1;
-    st.krem = (int32_t)r.krem;
-    st.K = r.K;
-    st.n = r.n;
-    st.m = 0;
-    st.T = 0;
-    st.keq = 0;
-  }
+  return r;
+}
+
+// Writes the group's selection state (and cnt[u] from KV head 0).
+__device__ inline void put_bounds(const SelectArgs& a, int ug, int u, int g, const SelBounds& r) {
+  SelState& st = a.st[ug];
+  st.b1 = r.b1;
+  st.krem = (int32_t)r.krem;
+  st.K = r.K;
+  st.n = r.n;
+  st.m = 0;
+  st.T = 0;
+  st.keq = 0;
+  if (g == 0) a.cnt[u] = r.K;
+}
+
+// The bounds alone, one wave per group: used when there are no selection tiles
+// (n_max = 0); otherwise k_sel_collect forms them itself.
+__global__ __launch_bounds__(64) void k_sel_thresh(SelectArgs a) {
+  const int ug = blockIdx.x;
+  const int u = ug / a.hkv, g = ug % a.hkv;
+  const SelBounds r = sel_bounds(a, ug, u, g == 0);
+  if (threadIdx.x == 0) put_bounds(a, ug, u, g, r);
 }
 
 // A selection tile's slots per thread: thread t takes the kSelTile / 256 consecutive
@@ -1476,20 +1573,32 @@ __device__ inline void load_slots(const float* row, int s0, int n_max, float (&x
 __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
   const int j = blockIdx.x % a.n_st;
+  const int u = ug / a.hkv, g = ug % a.hkv;
   const int tid = threadIdx.x;
   __shared__ uint32_t wtot[4];
-  // the tile's aggregates and the group's bounds, together
+  __shared__ int s_b1, s_n;
+  // the tile's aggregates, and (wave 0) the group's histogram, in flight together;
+  // every tile of the group forms the same bounds, tile 0 records them
   const int s0 = j * kSelTile + kSelSpt * tid;
   float x[kSelSpt];
   load_slots(a.agg + (size_t)ug * a.n_max, s0, a.n_max, x);
-  const SelState bd = a.st[ug];
+  if (tid < 64) {
+    const SelBounds r = sel_bounds(a, ug, u, g == 0 && j == 0);
+    if (tid == 0) {
+      s_b1 = r.b1;
+      s_n = r.n;
+      if (j == 0) put_bounds(a, ug, u, g, r);
+    }
+  }
+  __syncthreads();
+  const int b1 = s_b1, n = s_n;
   uint32_t gm = 0, cmk = 0;   // per-slot bits: above b1, in b1
 #pragma unroll
   for (int k = 0; k < kSelSpt; ++k) {
-    if (s0 + k < bd.n) {
+    if (s0 + k < n) {
       const int bin = lin_bin(x[k]);
-      gm |= (bin > bd.b1 ? 1u : 0u) << k;
-      cmk |= (bin == bd.b1 ? 1u : 0u) << k;
+      gm |= (bin > b1 ? 1u : 0u) << k;
+      cmk |= (bin == b1 ? 1u : 0u) << k;
     }
   }
   // the masks, for k_sel_emit (which then reads the aggregates of candidates only)
@@ -1694,7 +1803,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
 // The whole selection of one (unit, KV head) in one workgroup of 512 threads, for
 // rows of at most kSelGroupMax slots: thread t holds the aggregates of the 64
 // consecutive slots [64 t, 64 t + 64) in registers.  The histogram built by k_score
-// gives b1 and krem as in k_sel_thresh; three radix passes run straight over the
+// gives b1 and krem (sel_bounds); three radix passes run straight over the
 // thread's values of bin b1 (no candidate list); then per-thread counts of kept and
 // tied slots, two block scans, and the thread writes its kept slots in order.  Ties
 // at the threshold key are kept lowest slot first, as in the tile-parallel kernels.
@@ -1711,10 +1820,10 @@ __global__ __launch_bounds__(512) void k_sel_group(SelectArgs a) {
   const int ug = blockIdx.x;
   const int u = ug / a.hkv, g = ug % a.hkv;
   const int tid = threadIdx.x;
-  const bool lead = g == 0 && tid == 0;
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[2048];   // radix digits
   __shared__ uint32_t wtot[NT / 64];
   __shared__ uint32_t sh[2];
+  __shared__ SelBounds s_bd;
 
   // the thread's values, loaded first (16-byte loads, clamped inside the row)
   const float* row = a.agg + (size_t)ug * a.n_max;
@@ -1727,37 +1836,22 @@ __global__ __launch_bounds__(512) void k_sel_group(SelectArgs a) {
     for (int t = 0; t < 4; ++t) x[4 * i + t] = v[t];
   }
 
-  // bounds: n cached slots, K kept
-  const int n = clamp_len(a.len, u, a.n_max, lead ? a.flags : nullptr);
-  int B = a.budget[u];
-  const int prot = min(n, a.sink + a.window);
-  if (B < 0 || (n > B && B < prot)) {
-    if (lead) raise_flag(a.flags, kFlagBudget);
-    B = B < 0 ? 0 : B;
+  // bounds (wave 0): n cached slots, K kept, the bin b1 of the K-th largest
+  if (tid < 64) {
+    const SelBounds r = sel_bounds(a, ug, u, g == 0);
+    if (tid == 0) {
+      s_bd = r;
+      if (g == 0) a.cnt[u] = r.K;
+    }
   }
-  int K = B < n ? B : n;
-  if (K > a.b_max) {
-    if (lead) raise_flag(a.flags, kFlagBmax);
-    K = a.b_max;
-  }
-  if (lead) a.cnt[u] = K;
+  __syncthreads();
+  const int n = s_bd.n, K = s_bd.K, b1 = s_bd.b1;
 
   // the threshold: every slot of a bin above b1 is kept; in bin b1, keys above T and
   // the lowest keq slots equal to T
-  int b1;
   uint32_t T = 0, keq = 0;
-  if (K == 0) {
-    b1 = kBins;
-  } else if (K >= n) {
-    b1 = -1;
-  } else {
-    const uint32_t* gh = a.hist + (size_t)ug * kBins;
-    for (int i = tid; i < kBins; i += NT) hist[i] = gh[i];
-    __syncthreads();
-    uint32_t d, above;
-    find_digit<NT>(hist, kBins, (uint32_t)K, wtot, sh, d, above);
-    b1 = (int)d;
-    uint32_t krem = (uint32_t)K - above;
+  if (b1 >= 0 && b1 < kBins) {
+    uint32_t krem = s_bd.krem;
     uint32_t prefix = 0, pmask = 0;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
@@ -2335,13 +2429,10 @@ hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s) {
     return hipGetLastError();
   }
   const unsigned tiles = (unsigned)(groups * a.n_st);
-  hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(256), 0, s, a);
+  if (tiles) hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (tiles) {
-    hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   hipLaunchKernelGGL(k_sel_refine, dim3((unsigned)groups), dim3(512), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tiles) hipLaunchKernelGGL(k_sel_emit, dim3(tiles), dim3(256), 0, s, a);
