@@ -7,6 +7,10 @@ line.  Default workload: Qwen3-8B-shaped, 36 layers x 8 KV heads x 32768 keys.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config qwen3_8b]
 
+The default line also carries the Qwen3-32B-shaped pass under "extra_workloads"
+(--no-extra: the --config workload only).  With --read-probe GB it times the
+streaming-read probe (the practical read ceiling) instead of the pass.
+
 With --calibrate it times the calibration reduction instead (tria_calibrate over a
 Qwen3-8B-shaped stream of 8192 pre-RoPE query rows per layer and query head) and
 prints that measurement's JSON line.
@@ -43,53 +47,107 @@ def workload_desc(cfg) -> dict:
     return d
 
 
-def cpu_baseline(cfg, seconds: float) -> dict:
-    """The fp64 oracle as it stands, on a bounded sample of the same workload: whole
-    (unit, KV head) pairs in order until `seconds` of oracle time have passed."""
-    import numpy as np
+def _baseline_init():
+    """Pool worker set-up: one BLAS thread per process (the pool spans the cores)."""
     from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def _baseline_ready(_):
+    from key_importance_scoring_amd import synth  # noqa: F401  (imports paid before the clock starts)
+    from oracle import tria_oracle  # noqa: F401
+    return os.getpid()
+
+
+def _baseline_pairs(job):
+    """One worker's share: the oracle on each (unit, KV head) of `pairs`, timed around
+    the oracle's own steps only (input generation is outside the clock).  Returns
+    (keys, oracle seconds, pairs)."""
+    import numpy as np
     from key_importance_scoring_amd import synth
     from oracle import tria_oracle as o
 
+    cfg, pairs, form = job
     u = synth.units(cfg)
     re, im, ab = synth.q_stats(cfg)
     mu = re.astype(np.float64) + 1j * im.astype(np.float64)
     absm = ab.astype(np.float64)
     G = cfg.group
-    keys = 0
-    spent = 0.0
-    pairs = 0
-    with threadpool_limits(1):
-        for unit in range(cfg.n_units):
-            for g in range(cfg.n_kv_heads):
-                n = int(u.lengths[unit])
-                layer = int(u.unit_layer[unit])
-                k_bits = synth.key_rows(cfg, unit, g)
-                v_bits = synth.value_rows(cfg, unit, g)
-                pos = synth.positions(cfg, unit)
-                t0 = time.perf_counter()
-                rows = o.bf16_bits_to_f64(k_bits)
-                raw = np.stack([o.score_head(rows, pos, int(u.q_pos[unit]), mu[layer, h], absm[layer, h],
-                                             cfg.head_dim, cfg.pairing, cfg.rope_base, cfg.offsets, "folded",
-                                             cfg.offset_reduce)
-                                for h in range(g * G, (g + 1) * G)])
-                agg = o.aggregate_unit(raw, n, G, cfg.sink, cfg.window, cfg.agg)[0]
-                kept = o.select(agg, int(u.budget[unit]))
-                o.compact(k_bits, kept)
-                o.compact(v_bits, kept)
-                o.compact(pos, kept)
-                spent += time.perf_counter() - t0
-                keys += n
-                pairs += 1
-                if spent >= seconds:
-                    break
-            if spent >= seconds:
-                break
-    return {"value": keys / spent / 1e6, "unit": "M keys/s", "cores": 1, "kind": "oracle",
-            "sample": f"{pairs} (unit, KV head) pairs = {keys} keys of {cfg.name}, fp64 "
-                      f"{'direct form, maximum over offsets' if cfg.offset_reduce == 'max' else 'folded form'}, "
-                      f"{spent:.1f} s on one host thread",
+    keys, spent = 0, 0.0
+    for unit, g in pairs:
+        n = int(u.lengths[unit])
+        layer = int(u.unit_layer[unit])
+        k_bits = synth.key_rows(cfg, unit, g)
+        v_bits = synth.value_rows(cfg, unit, g)
+        pos = synth.positions(cfg, unit)
+        t0 = time.perf_counter()
+        rows = o.bf16_bits_to_f64(k_bits)
+        raw = np.stack([o.score_head(rows, pos, int(u.q_pos[unit]), mu[layer, h], absm[layer, h], cfg.head_dim,
+                                     cfg.pairing, cfg.rope_base, cfg.offsets, form, cfg.offset_reduce)
+                        for h in range(g * G, (g + 1) * G)])
+        agg = o.aggregate_unit(raw, n, G, cfg.sink, cfg.window, cfg.agg)[0]
+        kept = o.select(agg, int(u.budget[unit]))
+        o.compact(k_bits, kept)
+        o.compact(v_bits, kept)
+        o.compact(pos, kept)
+        spent += time.perf_counter() - t0
+        keys += n
+    return keys, spent, len(pairs)
+
+
+def host_cores() -> int:
+    """Host threads for the oracle pool: the cores this process may run on, at most 16
+    (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(cfg, seconds: float) -> dict:
+    """The fp64 oracle as it stands, on every host core (one process per core), on a
+    bounded sample of the same workload: whole (unit, KV head) pairs in order, as many
+    per worker as one worker gets through in about `seconds` of oracle time (from a
+    trial of one pair per worker, all workers at once).  Timed in both of its forms for the mean over offsets: the
+    folded dot product (`value`) and the direct per-offset sum; the maximum over
+    offsets has only the direct form.  A form's rate is all the keys over the slowest
+    worker's oracle time."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    workers = host_cores()
+    all_pairs = [(unit, g) for unit in range(cfg.n_units) for g in range(cfg.n_kv_heads)]
+    forms = ["direct"] if cfg.offset_reduce == "max" else ["folded", "direct"]
+    out = {}
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                                initializer=_baseline_init) as ex:
+        list(ex.map(_baseline_ready, range(workers)))
+        for form in forms:
+            # one pair per worker, all at once: the per-pair time under the same contention
+            trial = list(ex.map(_baseline_pairs, [(cfg, [all_pairs[w % len(all_pairs)]], form)
+                                                  for w in range(workers)]))
+            t_pair = max(r[1] for r in trial)
+            per = max(1, int(round(seconds / max(t_pair, 1e-3))))
+            take = [all_pairs[i % len(all_pairs)] for i in range(workers * per)]
+            jobs = [(cfg, take[w * per:(w + 1) * per], form) for w in range(workers)]
+            res = list(ex.map(_baseline_pairs, jobs))
+            keys = sum(r[0] for r in res)
+            slow = max(r[1] for r in res)
+            out[form] = {"value": keys / slow / 1e6, "pairs": sum(r[2] for r in res), "keys": keys,
+                         "slowest_worker_s": slow}
+    main_form = forms[0]
+    desc = {"folded": "folded form", "direct": "direct form"}
+    return {"value": out[main_form]["value"], "unit": "M keys/s", "cores": workers, "kind": "oracle",
+            "sample": f"{out[main_form]['pairs']} (unit, KV head) pairs = {out[main_form]['keys']} keys of "
+                      f"{cfg.name} ({per_note(out[main_form], workers)}), fp64 {desc[main_form]}"
+                      f"{', maximum over offsets' if cfg.offset_reduce == 'max' else ''}, one process per core",
+            "forms": {f: dict(v, unit="M keys/s") for f, v in out.items()},
             "host_cpus": os.cpu_count()}
+
+
+def per_note(r: dict, workers: int) -> str:
+    return f"{r['pairs'] // workers} per worker, slowest worker {r['slowest_worker_s']:.1f} s of oracle time"
 
 
 def recorded_traffic(kernel: str, workload: str):
@@ -135,6 +193,50 @@ def copy_probe(gb: float, steps: int) -> int:
     ms = t0.elapsed_time(t1) / steps
     print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
                       "GBps_read_plus_write": 2 * n / (ms / 1e3) / 1e9}))
+    return 0
+
+
+def read_probe(args) -> int:
+    """The streaming-read probe (libtria_probe.so): `--read-probe` GB read once per step
+    by a persistent grid of `--probe-wgs-per-cu` workgroups per compute unit in tiles of
+    `--probe-tile-kib` KiB, the score kernel's access shape.  Its rate is the practical
+    read ceiling the score kernel is compared with."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "key_importance_scoring_amd", "libtria_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run python -m key_importance_scoring_amd.build")
+    lib = ctypes.CDLL(path)
+    lib.tria_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    lib.tria_probe_read.restype = ctypes.c_int
+    n = int(args.read_probe * 1e9) // 16 * 16
+    tile = args.probe_tile_kib * 1024
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = args.probe_wgs_per_cu * cus
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(0x5A)
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.tria_probe_read(src.data_ptr(), n, tile, grid, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"tria_probe_read failed: {rc}")
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        launch()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"probe": "read", "kernel": "k_read_probe", "bytes_read": n, "tile_bytes": tile, "grid": grid,
+                      "compute_units": cus, "steps": args.steps, "ms": ms, "GBps_read": n / (ms / 1e3) / 1e9,
+                      "frac_of_hbm_peak": n / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}))
     return 0
 
 
@@ -372,6 +474,13 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GB",
                     help="instead of the pass, time a plain device-to-device copy of GB gigabytes "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--read-probe", type=float, default=0.0, metavar="GB",
+                    help="instead of the pass, time the streaming-read probe over GB gigabytes (2.415919104: "
+                         "the Qwen3-8B-shaped K cache)")
+    ap.add_argument("--probe-tile-kib", type=int, default=512, help="read probe tile (KiB; default 512)")
+    ap.add_argument("--probe-wgs-per-cu", type=int, default=2, help="read probe workgroups per compute unit")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="time only --config (the default Qwen3-8B line also times the Qwen3-32B-shaped pass)")
     ap.add_argument("--calibrate", action="store_true",
                     help="instead of the pass, time the calibration reduction (tria_calibrate) over a "
                          "synthetic pre-RoPE query stream of --tokens rows per (layer, query head)")
@@ -396,18 +505,77 @@ def main() -> int:
     import torch
     if args.copy_probe > 0:
         return copy_probe(args.copy_probe, args.steps)
+    if args.read_probe > 0:
+        return read_probe(args)
     if args.calibrate:
         return bench_calibrate(args)
     if args.decode_loop:
         return bench_decode(args)
     from key_importance_scoring_amd import _lib as L
     from key_importance_scoring_amd import synth
-    from key_importance_scoring_amd.device import DeviceProblem
 
+    L.tria_select_strategy({"auto": L.SELECT_AUTO, "per_group": L.SELECT_PER_GROUP,
+                            "tiled": L.SELECT_TILED}[args.select])
     cfg = synth.CONFIGS[args.config]
-    cache_name = cfg.name          # the offset reduction does not change the inputs
     if args.offsets == "max":
         cfg = cfg.replace(name=f"{cfg.name}_offsets_max", offset_reduce="max")
+    r = time_pass(cfg, args)
+    extra = {}
+    # the default line also carries the Qwen3-32B-shaped pass (same steps and warmup)
+    if args.extra and args.config == "qwen3_8b" and args.offsets == "mean":
+        for name in ("qwen3_32b",):
+            e = time_pass(synth.CONFIGS[name], args)
+            extra[name] = {"value": e["value"], "unit": "M keys/s", "ms_per_step": e["ms"],
+                           "hbm_algorithmic_GBps": e["alg_GBps"], "hbm_pct_of_peak": e["pct"],
+                           "algorithmic_bytes_per_step": e["alg"], "head_keys_per_step": e["keys"],
+                           "kernel_ms": e["per_kernel"], "roofline": e["roofline"],
+                           "config": workload_desc(synth.CONFIGS[name])}
+
+    base = None
+    if args.cpu_seconds > 0:
+        print(f"[bench] oracle CPU baseline ({host_cores()} processes)", file=sys.stderr, flush=True)
+        base = cpu_baseline(cfg, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "M keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(workload_desc(cfg), **({"select": args.select} if args.select != "auto" else {})),
+        "hbm_algorithmic_GBps": r["alg_GBps"],
+        "hbm_pct_of_peak": r["pct"],
+        "algorithmic_bytes_per_step": r["alg"],
+        "head_keys_per_step": r["keys"],
+        "kernel_ms": r["per_kernel"],
+        "kernel_timing": {"source": "HIP events on the launch stream around each library launch, over a second "
+                                    "region of the same K steps after the timed one",
+                          "ms_per_step_with_kernel_events": r["ms_inst"]},
+        "roofline": r["roofline"],
+        "cpu_baseline": base,
+    }
+    if extra:
+        out["extra_workloads"] = extra
+    print(json.dumps(out))
+    return 0
+
+
+def time_pass(cfg, args) -> dict:
+    """Builds cfg's inputs on the device, runs W warmup steps, then times K steps twice:
+    once bare (the measurement) and once with HIP events around every library launch
+    (per-kernel times).  The device buffers are released before it returns."""
+    import torch
+    from key_importance_scoring_amd import _lib as L
+    from key_importance_scoring_amd.device import DeviceProblem
+
+    cache_name = cfg.name.replace("_offsets_max", "")   # the offset reduction does not change the inputs
     print(f"[bench] building {cfg.name} inputs", file=sys.stderr, flush=True)
     hosts = {}
     if args.input_cache:
@@ -425,9 +593,7 @@ def main() -> int:
     prob = DeviceProblem(cfg, device="cuda:0", keep_raw=False, k_host=hosts.get("k"), v_host=hosts.get("v"))
     hosts.clear()
     stream = torch.cuda.current_stream()
-    L.tria_select_strategy({"auto": L.SELECT_AUTO, "per_group": L.SELECT_PER_GROUP,
-                            "tiled": L.SELECT_TILED}[args.select])
-    print("[bench] warmup", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name} warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         prob.run(stream)
     torch.cuda.synchronize()
@@ -471,46 +637,22 @@ def main() -> int:
     score_flops = keys * cfg.group * 2 * (cfg.head_dim * dots + cfg.head_dim // 2)
     score_ms = per_kernel["k_score"]
     achieved = score_bytes / (score_ms / 1e3) / 1e9
-    print(f"[bench] {ms:.3f} ms/step ({ms_inst:.3f} with per-kernel events), wall {wall / args.steps * 1e3:.3f} "
-          f"ms/step, kernels {per_kernel}", file=sys.stderr, flush=True)
-
-    base = None
-    if args.cpu_seconds > 0:
-        print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
-        base = cpu_baseline(cfg, args.cpu_seconds)
-
-    out = {
-        "metric": METRIC,
+    print(f"[bench] {cfg.name}: {ms:.3f} ms/step ({ms_inst:.3f} with per-kernel events), wall "
+          f"{wall / args.steps * 1e3:.3f} ms/step, kernels {per_kernel}", file=sys.stderr, flush=True)
+    del prob
+    torch.cuda.empty_cache()
+    return {
+        "ms": ms, "ms_inst": ms_inst, "keys": keys, "alg": alg, "per_kernel": per_kernel,
         "value": keys / (ms / 1e3) / 1e6,
-        "unit": "M keys/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": dict(workload_desc(cfg), **({"select": args.select} if args.select != "auto" else {})),
-        "hbm_algorithmic_GBps": alg / (ms / 1e3) / 1e9,
-        "hbm_pct_of_peak": 100.0 * alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
-        "algorithmic_bytes_per_step": alg,
-        "head_keys_per_step": keys,
-        "kernel_ms": per_kernel,
-        "kernel_timing": {"source": "HIP events on the launch stream around each library launch, over a second "
-                                    "region of the same K steps after the timed one",
-                          "ms_per_step_with_kernel_events": ms_inst},
+        "alg_GBps": alg / (ms / 1e3) / 1e9,
+        "pct": 100.0 * alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"kernel": score_kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(score_kernel, cfg.name),
                      "algorithmic_bytes_per_launch": score_bytes, "dominant_kernel": dom,
                      "mfma_bf16_tflops": score_flops / (score_ms / 1e3) / 1e12,
                      "mfma_frac_of_bf16_dense_peak": score_flops / (score_ms / 1e3) / 2.5e15},
-        "cpu_baseline": base,
     }
-    print(json.dumps(out))
-    return 0
 
 
 if __name__ == "__main__":
