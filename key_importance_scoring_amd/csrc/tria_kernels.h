@@ -16,6 +16,9 @@ constexpr int kMaxGroup = 8;
 constexpr int kListUnits = 512;
 constexpr int kScoreTileMax = 2048;
 // keys per score tile: two tiles of scores ([G][tile + 16] fp32 each) live in LDS
+#ifndef TRIA_SCORE_TILE_LARGE_G
+#define TRIA_SCORE_TILE_LARGE_G 1024
+#endif
 #ifndef TRIA_SCORE_TILE_SMALL_G
 #define TRIA_SCORE_TILE_SMALL_G 2048
 #endif
@@ -26,7 +29,7 @@ constexpr int kScoreTileMax = 2048;
 // in 64-key stages), so that a row just past a multiple of the cap is not followed
 // by a nearly empty tile.
 inline int score_tile_keys(int group, int omax, int n_max) {
-  const int cap = group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : 1024;
+  const int cap = group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : TRIA_SCORE_TILE_LARGE_G;
   if (n_max <= cap) return cap;
   const int nt = (n_max + cap - 1) / cap;
   const int t = ((n_max + nt - 1) / nt + 255) / 256 * 256;
@@ -156,6 +159,11 @@ struct SelState {
 constexpr int kSelTile = TRIA_SEL_TILE; // slots per selection tile (kSelTile / 256 per thread)
 constexpr int kSelGroupMax = 32768;     // per-group selection: 512 threads x 64 slots in registers
 constexpr int kRefineLds = 3072;        // candidates the refinement keeps in LDS
+#ifndef TRIA_SEL_RANK_MAX
+#define TRIA_SEL_RANK_MAX 256
+#endif
+constexpr int kSelRankMax = TRIA_SEL_RANK_MAX;   // up to this many candidates: ranks instead of radix passes
+static_assert(kSelRankMax <= 512, "one candidate per thread of the 512-thread refinement");
 constexpr int kMaxSelTiles = 2048;      // per (unit, KV head): n_max <= 2048 kSelTile
 
 // A selection tile's per-thread bit masks: bit k stands for slot s0 + k of the

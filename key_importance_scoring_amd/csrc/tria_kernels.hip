@@ -1403,17 +1403,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // ============================================================================ selection
 // tria_select keeps, per (unit, KV head), the K = min(B, n) slots with the largest
-// aggregates (ties to the lower slot), in three steps; the two tile-parallel steps
-// carry all the per-slot work, the per-group step touches only a short candidate
-// list and per-tile counts:
-//   k_sel_collect (per tile)  wave 0 finds, in the histogram of the aggregates'
-//                 linear bins that k_score built, the bin b1 holding the K-th
-//                 largest (the binning is monotone, so every slot in a higher bin is
-//                 kept and every slot in a lower bin dropped) while the tile's
-//                 aggregates load; then the tile counts its slots above b1 and lists
-//                 its slots of b1 in its own segment of the group's candidate list;
+// aggregates (ties to the lower slot), in four steps; the two tile-parallel steps
+// carry all the per-slot work, the per-group steps touch only histograms, a short
+// candidate list and per-tile counts:
+//   k_sel_thresh  (per group, one wave) the histogram of the aggregates' linear
+//                 bins, built by k_score, gives the bin b1 holding the K-th largest;
+//                 the binning is monotone, so every slot in a higher bin is kept and
+//                 every slot in a lower bin dropped;
+//   k_sel_collect (per tile)  counts the tile's slots above b1 and lists its slots of
+//                 b1 in the tile's own segment of the group's candidate list;
 //   k_sel_refine  (per group) exact radix passes (11 + 11 + 10 bits of the
-//                 order-preserving key) over the candidates give the threshold key T
+//                 order-preserving key) over the candidates, or for at most
+//                 kSelRankMax candidates each one's rank among them, give the threshold key T
 //                 and how many slots equal to T are kept (the lowest ones); then each
 //                 tile's output offset and share of the tied slots;
 //   k_sel_emit    (per tile)  writes the tile's kept slots in ascending order.
@@ -1454,8 +1455,9 @@ __device__ inline void find_digit(const uint32_t* hist, int nb, uint32_t krem, u
 
 // The selection's bounds for group ug: n cached slots, K kept, and the bin b1
 // holding the K-th largest aggregate (-1: keep everything; kBins: keep nothing) with
-// krem slots still to take from it.  Formed by one wave (every lane returns the same
-// values): lane l holds the kSelPL consecutive bins from kSelPL l, an inclusive scan
+// krem slots still to take from it.  Formed by one wave from the group's kBins bins
+// (`bins`: a copy in LDS, or the histogram itself), every lane returning the same
+// values: lane l holds the kSelPL consecutive bins from kSelPL l, an inclusive scan
 // from the top lane down gives each lane the count in its bins and above, the lane
 // where that count first reaches K walks its own bins from the top.  A histogram
 // holding fewer than K slots (len changed since tria_score, outside the contract)
@@ -1466,14 +1468,11 @@ struct SelBounds {
   uint32_t krem;
 };
 
-__device__ inline SelBounds sel_bounds(const SelectArgs& a, int ug, int u, bool lead) {
+__device__ inline SelBounds sel_bounds(const SelectArgs& a, const uint32_t* bins, int u, bool lead) {
   const int lane = threadIdx.x & 63;
   uint32_t h[kSelPL];
-  {
-    const uint32_t* gh = a.hist + (size_t)ug * kBins + kSelPL * lane;
 #pragma unroll
-    for (int i = 0; i < kSelPL; ++i) h[i] = kSelPL * lane + i < kBins ? gh[i] : 0u;
-  }
+  for (int i = 0; i < kSelPL; ++i) h[i] = kSelPL * lane + i < kBins ? bins[kSelPL * lane + i] : 0u;
   int32_t* flags = lead && lane == 0 ? a.flags : nullptr;
   SelBounds r;
   r.n = clamp_len(a.len, u, a.n_max, flags);
@@ -1544,13 +1543,26 @@ __device__ inline void put_bounds(const SelectArgs& a, int ug, int u, int g, con
   if (g == 0) a.cnt[u] = r.K;
 }
 
-// The bounds alone, one wave per group: used when there are no selection tiles
-// (n_max = 0); otherwise k_sel_collect forms them itself.
+// One wave per group: the histogram, loaded coalesced into LDS (every load in
+// flight at once), then the bounds, recorded for the other selection kernels.
 __global__ __launch_bounds__(64) void k_sel_thresh(SelectArgs a) {
+  constexpr int NL = (kBins + 63) / 64;
   const int ug = blockIdx.x;
   const int u = ug / a.hkv, g = ug % a.hkv;
-  const SelBounds r = sel_bounds(a, ug, u, g == 0);
-  if (threadIdx.x == 0) put_bounds(a, ug, u, g, r);
+  const int lane = threadIdx.x;
+  __shared__ uint32_t s_bins[kBins];
+  {
+    const uint32_t* gh = a.hist + (size_t)ug * kBins;
+    uint32_t hb[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) hb[i] = lane + 64 * i < kBins ? gh[lane + 64 * i] : 0u;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (lane + 64 * i < kBins) s_bins[lane + 64 * i] = hb[i];
+  }
+  __syncthreads();
+  const SelBounds r = sel_bounds(a, s_bins, u, g == 0);
+  if (lane == 0) put_bounds(a, ug, u, g, r);
 }
 
 // A selection tile's slots per thread: thread t takes the kSelTile / 256 consecutive
@@ -1573,25 +1585,14 @@ __device__ inline void load_slots(const float* row, int s0, int n_max, float (&x
 __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
   const int j = blockIdx.x % a.n_st;
-  const int u = ug / a.hkv, g = ug % a.hkv;
   const int tid = threadIdx.x;
   __shared__ uint32_t wtot[4];
-  __shared__ int s_b1, s_n;
-  // the tile's aggregates, and (wave 0) the group's histogram, in flight together;
-  // every tile of the group forms the same bounds, tile 0 records them
+  // the tile's aggregates and the group's bounds, together
   const int s0 = j * kSelTile + kSelSpt * tid;
   float x[kSelSpt];
   load_slots(a.agg + (size_t)ug * a.n_max, s0, a.n_max, x);
-  if (tid < 64) {
-    const SelBounds r = sel_bounds(a, ug, u, g == 0 && j == 0);
-    if (tid == 0) {
-      s_b1 = r.b1;
-      s_n = r.n;
-      if (j == 0) put_bounds(a, ug, u, g, r);
-    }
-  }
-  __syncthreads();
-  const int b1 = s_b1, n = s_n;
+  const SelState bd = a.st[ug];
+  const int b1 = bd.b1, n = bd.n;
   uint32_t gm = 0, cmk = 0;   // per-slot bits: above b1, in b1
 #pragma unroll
   for (int k = 0; k < kSelSpt; ++k) {
@@ -1630,7 +1631,7 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   __shared__ uint32_t sh[2];
   __shared__ int32_t s_gtb[kMaxSelTiles], s_eqc[kMaxSelTiles];
   __shared__ int32_t s_pre[kMaxSelTiles + 1];   // candidates before each tile's segment
-  __shared__ uint32_t s_key[kRefineLds];        // candidates' order keys and slots, when
+  __shared__ __attribute__((aligned(16))) uint32_t s_key[kRefineLds];   // candidates' order keys and slots, when
   __shared__ int32_t s_slot[kRefineLds];        // they fit (else read again per pass)
 
   const SelState bd = a.st[ug];
@@ -1681,7 +1682,41 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   __syncthreads();
   auto cand_slot = [&](int i) { return staged ? s_slot[i] : cand(i); };
   auto cand_key = [&](int i) { return staged ? s_key[i] : order_key(row[cand(i)]); };
-  if (refine) {
+  if (refine && staged && m <= kSelRankMax) {
+    // few candidates: candidate i's key is the threshold T when fewer than krem keys
+    // lie above it and at least krem at or above it; keq = krem - (keys above T).
+    // (No candidate qualifies only for a histogram inconsistent with the scores:
+    // T = 0, keq = 0 then.)
+    __shared__ uint32_t s_tk[2];
+    if (tid == 0) s_tk[0] = s_tk[1] = 0u;
+    __syncthreads();
+    const uint32_t krem = (uint32_t)bd.krem;
+    if (tid < m) {
+      const uint32_t k = s_key[tid];
+      uint32_t gt = 0, ge = 0;
+      const int m4 = m & ~3;
+#pragma unroll 4
+      for (int i = 0; i < m4; i += 4) {   // every lane reads the same 16 bytes: a broadcast
+        const u32x4 o = *reinterpret_cast<const u32x4*>(s_key + i);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          gt += o[t] > k ? 1u : 0u;
+          ge += o[t] >= k ? 1u : 0u;
+        }
+      }
+      for (int i = m4; i < m; ++i) {
+        gt += s_key[i] > k ? 1u : 0u;
+        ge += s_key[i] >= k ? 1u : 0u;
+      }
+      if (gt < krem && krem <= ge) {   // every such candidate holds the same key
+        s_tk[0] = k;
+        s_tk[1] = krem - gt;
+      }
+    }
+    __syncthreads();
+    T = s_tk[0];
+    keq = s_tk[1];
+  } else if (refine) {
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)bd.krem;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
@@ -1838,7 +1873,7 @@ __global__ __launch_bounds__(512) void k_sel_group(SelectArgs a) {
 
   // bounds (wave 0): n cached slots, K kept, the bin b1 of the K-th largest
   if (tid < 64) {
-    const SelBounds r = sel_bounds(a, ug, u, g == 0);
+    const SelBounds r = sel_bounds(a, a.hist + (size_t)ug * kBins, u, g == 0);
     if (tid == 0) {
       s_bd = r;
       if (g == 0) a.cnt[u] = r.K;
@@ -2429,10 +2464,13 @@ hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s) {
     return hipGetLastError();
   }
   const unsigned tiles = (unsigned)(groups * a.n_st);
-  if (tiles) hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_sel_thresh, dim3((unsigned)groups), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (tiles) {
+    hipLaunchKernelGGL(k_sel_collect, dim3(tiles), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_sel_refine, dim3((unsigned)groups), dim3(512), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (tiles) hipLaunchKernelGGL(k_sel_emit, dim3(tiles), dim3(256), 0, s, a);
