@@ -399,7 +399,7 @@ tria_status tria_pass_noalloc(const tria_params* p, const tria_kv_view* k, const
                               int32_t pos_heads, float* agg, int32_t* idx, int32_t* cnt, const tria_kv_view* k_dst,
                               const tria_kv_view* v_dst, int32_t* pos_dst, int32_t* flags, void* stream);
 
-/* Polls of tria_score's bounded wait for a group's tile moments (the default,
+/* Polls of tria_score's bounded wait for a group's merged moments (the default,
  * 65536, is ~0.1-0.2 s).  When a wait runs out, the workgroup computes the group's
  * moments directly from the K cache instead (TRIA_FLAG_SYNC is raised as
  * information).  A negative value skips the exchange altogether: every
@@ -419,6 +419,15 @@ int32_t tria_score_wait_polls(int32_t polls);
  * Process-wide; returns the previous strategy (an unknown value selects AUTO). */
 typedef enum { TRIA_SELECT_AUTO = 0, TRIA_SELECT_PER_GROUP = 1, TRIA_SELECT_TILED = 2 } tria_select_strategy_t;
 int32_t tria_select_strategy(int32_t strategy);
+
+/* Host decision log: one line per entry-point call on stderr, prefixed "[tria] ",
+ * naming what the host chose (kernel variant, tile size and count, grid, LDS bytes,
+ * selection strategy, compaction variant, workspace use), plus one line for every
+ * error an entry point returns (status, name, detail).  Off unless the environment
+ * variable TRIA_LOG is set to anything but "" or "0" when the library first logs.
+ * tria_log(1) turns it on, tria_log(0) off, a negative value only queries.
+ * Process-wide; returns the previous state (0 or 1). */
+int32_t tria_log(int32_t on);
 
 /* Reads (after synchronising `stream`) and clears the device flag word of a
  * workspace.  Returns TRIA_OK and the OR of TRIA_FLAG_* in *flags. */

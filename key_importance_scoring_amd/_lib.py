@@ -25,7 +25,7 @@ FLAG_LEN, FLAG_LAYER, FLAG_BUDGET, FLAG_BLOCK, FLAG_INDEX, FLAG_BMAX, FLAG_SYNC 
 
 EXPORTS = ("tria_workspace_size", "tria_score", "tria_select", "tria_compact", "tria_device_flags",
            "tria_strerror", "tria_last_error", "tria_timing_enable", "tria_timing_read", "tria_kernel_name",
-           "tria_score_max_workgroups", "tria_score_wait_polls", "tria_select_strategy",
+           "tria_score_max_workgroups", "tria_score_wait_polls", "tria_log", "tria_select_strategy",
            "tria_calibrate_workspace_size",
            "tria_calibrate", "tria_compact_inplace", "tria_append", "tria_stats_parse", "tria_stats_encode",
            "tria_stats_band_mask", "tria_stats_layer_budgets", "tria_pass_noalloc")
@@ -102,6 +102,8 @@ def load() -> ctypes.CDLL:
     lib.tria_score_max_workgroups.argtypes = [c_int32]
     lib.tria_score_wait_polls.restype = c_int32
     lib.tria_score_wait_polls.argtypes = [c_int32]
+    lib.tria_log.restype = c_int32
+    lib.tria_log.argtypes = [c_int32]
     lib.tria_select_strategy.restype = c_int32
     lib.tria_select_strategy.argtypes = [c_int32]
     lib.tria_calibrate_workspace_size.restype = c_size_t
@@ -262,6 +264,11 @@ def tria_score_wait_polls(polls: int) -> int:
     """Sets tria_score's bounded wait for a group's moments (< 0: compute them directly
     every time); returns the previous value."""
     return int(load().tria_score_wait_polls(int(polls)))
+
+
+def tria_log(on: int) -> int:
+    """The host decision log on stderr (1 on, 0 off, < 0 query); returns the previous state."""
+    return int(load().tria_log(int(on)))
 
 
 def tria_timing_enable(on: bool) -> int:

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <atomic>
 #include <mutex>
@@ -18,6 +19,34 @@
 
 namespace {
 
+// ------------------------------------------------------------------ log
+// The host's decisions (tile sizes, grids, kernel variants, strategies) and every
+// error an entry point returns, one line each on stderr, prefixed "[tria] ".  On when
+// the environment variable TRIA_LOG holds anything but "" or "0" at the first call
+// that logs, or after tria_log(1).
+std::atomic<int> g_log{-1};
+
+bool log_on() {
+  int v = g_log.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("TRIA_LOG");
+    int want = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    g_log.compare_exchange_strong(v, want);
+    v = g_log.load(std::memory_order_relaxed);
+  }
+  return v > 0;
+}
+
+void tlog(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[768];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[tria] %s\n", buf);
+}
+
 thread_local char g_err[512] = "";
 
 tria_status fail(tria_status s, const char* fmt, ...) {
@@ -25,8 +54,12 @@ tria_status fail(tria_status s, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
+  tlog("error %d (%s): %s", (int)s, tria_strerror(s), g_err);
   return s;
 }
+
+const char* pairing_name(int p) { return p == TRIA_PAIR_NEOX ? "NEOX" : "interleaved"; }
+const char* layout_name(const tria_kv_view* v) { return v->block_table ? "paged" : "dense"; }
 
 }  // namespace
 
@@ -253,6 +286,19 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
   if (wg_cap > 0 && L.n_tiles > wg_cap)
     return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the workgroup cap is %d",
                 n_max, L.n_tiles, wg_cap);
+  if (log_on()) {
+    const long tiles = (long)n_units * p->n_kv_heads * L.n_tiles;
+    const int grid_cap = wg_cap > 0 && wg_cap < cap ? wg_cap : cap;
+    tlog("score: %d units x %d KV heads x n_max %d, d %d, G %d, %s, %s K, %d offsets (%s), %s aggregation: "
+         "%s, tiles of %d keys (%d per (unit, KV head), %ld in all), grid %ld (resident capacity %d, cap %d), "
+         "LDS %zu B, moment wait %d polls, workspace %zu of %zu B",
+         n_units, p->n_kv_heads, n_max, p->head_dim, p->group, pairing_name(p->pairing), layout_name(k),
+         p->n_offsets, omax ? "maximum" : "mean", p->agg == TRIA_AGG_MAX ? "max" : "mean",
+         omax ? "k_score_max" : "k_score", L.tile, L.n_tiles, tiles, tiles < grid_cap ? tiles : (long)grid_cap, cap,
+         wg_cap, tria::score_lds(p->head_dim, p->group, k->block_table != nullptr, omax, L.ob.nblk, L.tile,
+                                 k->block_size),
+         g_wait_polls.load(), L.total, ws_bytes);
+  }
   if (dry) return TRIA_OK;
 
   char* w = static_cast<char*>(ws);
@@ -305,6 +351,18 @@ tria_status select_impl(const tria_params* p, int32_t n_units, int32_t n_max, in
   char* w = static_cast<char*>(ws);
   if (L.n_st > tria::kMaxSelTiles)
     return fail(TRIA_ESHAPE, "n_max %d exceeds the selection's %d tiles", n_max, tria::kMaxSelTiles);
+  if (log_on()) {
+    const int strategy = g_select_strategy.load();
+    const bool per_group = strategy == TRIA_SELECT_PER_GROUP && n_max <= tria::kSelGroupMax;
+    if (per_group)
+      tlog("select: %d units x %d KV heads, n_max %d, b_max %d: k_sel_group (one workgroup per (unit, KV head))",
+           n_units, p->n_kv_heads, n_max, b_max);
+    else
+      tlog("select: %d units x %d KV heads, n_max %d, b_max %d: k_sel_thresh, k_sel_collect, k_sel_refine "
+           "(ranks up to %d candidates, else radix passes), k_sel_emit; %d selection tiles of %d slots per row%s",
+           n_units, p->n_kv_heads, n_max, b_max, tria::kSelRankMax, L.n_st, tria::kSelTile,
+           strategy == TRIA_SELECT_PER_GROUP ? " (per-group requested; the row exceeds its limit)" : "");
+  }
   if (dry) return TRIA_OK;
   int32_t* tiles = reinterpret_cast<int32_t*>(w + L.tiles);
   const size_t nt = (size_t)n_units * p->n_kv_heads * L.n_st;
@@ -363,6 +421,18 @@ tria_status compact_impl(const tria_params* p, const tria_kv_view* k_src, const 
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(pos_dst);
     const uintptr_t d1 = d0 + (size_t)n_units * hkv * b_max * 4;
     if (overlaps(s0, s1, d0, d1)) return fail(TRIA_EOVERLAP, "pos_dst overlaps pos_src");
+  }
+  if (log_on()) {
+    auto same_table = [](const tria_kv_view* x, const tria_kv_view* y) {
+      return x->block_table == y->block_table &&
+             (!x->block_table || (x->block_size == y->block_size && x->max_blocks == y->max_blocks &&
+                                  x->n_pool_blocks == y->n_pool_blocks));
+    };
+    const bool fast = same_table(k_src, v_src) && same_table(k_dst, v_dst);
+    tlog("compact: %d units x %d KV heads, n_max %d, b_max %d, %s -> %s: %s (%d rows per workgroup)%s", n_units,
+         hkv, n_max, b_max, layout_name(k_src), layout_name(k_dst),
+         fast ? "k_compact_fast" : "k_compact (K and V in different layouts: one row at a time)", tria::kCompactRows,
+         pos_src && pos_dst ? ", positions" : "");
   }
   if (dry) return TRIA_OK;
 
@@ -426,6 +496,9 @@ tria_status tria_calibrate(const tria_params* p, const void* q, int64_t stride_l
   const size_t need = tria_calibrate_workspace_size(p, n_tokens);
   if (ws_bytes < need) return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   const int32_t n_chunks = (n_tokens + tria::kCalibChunk - 1) / tria::kCalibChunk;
+  tlog("calibrate: %d layers x %d query heads x %d tokens, d %d, %s: k_calib over %d chunks of %d tokens, "
+       "then k_calib_final", p->n_layers, p->n_kv_heads * p->group, n_tokens, p->head_dim, pairing_name(p->pairing),
+       n_chunks, tria::kCalibChunk);
   tria::CalibArgs ca{static_cast<const uint16_t*>(q), stride_layer, stride_head, stride_token, p->n_layers,
                      p->n_kv_heads * p->group, p->head_dim, p->pairing, n_tokens, n_chunks,
                      static_cast<float*>(ws), q_mean_re, q_mean_im, q_abs_mean, r, mrl};
@@ -451,6 +524,8 @@ tria_status tria_compact_inplace(const tria_params* p, const tria_kv_view* k, co
     dense_range(v, n_units, p->n_kv_heads, n_max, p->head_dim, b0, b1);
     if (overlaps(a0, a1, b0, b1)) return fail(TRIA_EOVERLAP, "k and v overlap");
   }
+  tlog("compact_inplace: %d units x %d KV heads, n_max %d, b_max %d, %s: k_compact_inplace, then len <- cnt",
+       n_units, p->n_kv_heads, n_max, b_max, layout_name(k));
   tria::InplaceArgs ia{mkview(k), mkview(v), pos, n_units, n_max, b_max, p->n_kv_heads, p->head_dim,
                        len, idx, cnt, static_cast<int32_t*>(ws)};
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -471,6 +546,8 @@ tria_status tria_append(const tria_params* p, const tria_kv_view* k, const tria_
     return fail(TRIA_ESHAPE, "k_new and v_new must be 16-byte aligned");
   if (!ws) return fail(TRIA_EWORKSPACE, "workspace is NULL (its flag word records contract violations)");
   if (n_units == 0 || t_new == 0) return TRIA_OK;
+  tlog("append: %d units x %d KV heads, %d new rows each, n_max %d, %s: k_append%s", n_units, p->n_kv_heads,
+       t_new, n_max, layout_name(k), q_pos ? ", then len += t_new and q_pos <- the newest position" : ", then len += t_new");
   tria::AppendArgs aa{mkview(k), mkview(v), pos, n_units, n_max, p->n_kv_heads, p->head_dim, t_new, len, q_pos,
                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), pos_new,
                       static_cast<int32_t*>(ws)};
@@ -495,6 +572,7 @@ tria_status tria_pass_noalloc(const tria_params* p, const tria_kv_view* k, const
   void* ws = tria::scratch_address(&e);
   if (!ws) return fail(TRIA_ELAUNCH, "scratch address: %s", hipGetErrorString(e));
   const size_t wsb = tria::kScratchBytes;
+  tlog("pass_noalloc: workspace %zu of the %zu B static scratch at %p", need, wsb, ws);
   // every step's checks before anything is launched
   if ((st = score_impl(p, k, n_units, n_max, len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean, nullptr, agg,
                        ws, wsb, stream, true)) != TRIA_OK ||
@@ -558,6 +636,12 @@ int32_t tria_score_max_workgroups(int32_t cap) {
 
 int32_t tria_score_wait_polls(int32_t polls) {
   return g_wait_polls.exchange(polls < 0 ? -1 : polls);
+}
+
+int32_t tria_log(int32_t on) {
+  const int prev = log_on() ? 1 : 0;
+  if (on >= 0) g_log.store(on > 0 ? 1 : 0);
+  return prev;
 }
 
 int32_t tria_timing_enable(int32_t on) {

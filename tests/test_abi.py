@@ -313,3 +313,46 @@ def test_pass_noalloc_checks():
     assert L.tria_workspace_size(p, 300, 32768) > 96 << 20
     assert _status(lambda: call(n_units=300, n_max=32768)) == L.TRIA_EWORKSPACE
     assert "scratch holds" in L.load().tria_last_error().decode()
+
+
+def test_log_switch_is_process_wide_and_returns_previous():
+    prev = L.tria_log(-1)
+    try:
+        L.tria_log(1)
+        assert L.tria_log(-1) == 1          # a negative value only queries
+        assert L.tria_log(0) == 1
+        assert L.tria_log(-1) == 0
+    finally:
+        L.tria_log(prev)
+
+
+def test_log_reports_each_error_once_on_stderr(capfd):
+    prev = L.tria_log(1)
+    try:
+        capfd.readouterr()
+        assert _status(lambda: _score(n_max=4100)) == L.TRIA_ESHAPE
+        err = capfd.readouterr().err
+        lines = [l for l in err.splitlines() if l.startswith("[tria] ")]
+        assert len(lines) == 1 and "error" in lines[0] and "multiple of 16" in lines[0], err
+        L.tria_log(0)
+        assert _status(lambda: _score(n_max=4100)) == L.TRIA_ESHAPE
+        assert "[tria]" not in capfd.readouterr().err
+    finally:
+        L.tria_log(prev)
+
+
+@pytest.mark.parametrize("value,on", [("1", True), ("0", False), ("", False)])
+def test_log_follows_the_environment(value, on):
+    import subprocess
+    import sys
+    code = ("import key_importance_scoring_amd as kis\n"
+            "from key_importance_scoring_amd import _lib as L\n"
+            "p = L.make_params(128, 8, 4, 2, L.PAIR_NEOX, L.AGG_MAX, 1e6, [1, 2], 0, 0)\n"
+            "try:\n"
+            "    L.tria_select(p, 1, 100, 8, 1, 1, 1, 1, 1, None, 0)\n"
+            "except kis.TriaError:\n"
+            "    pass\n")
+    env = dict(os.environ, TRIA_LOG=value, PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert ("[tria] error" in r.stderr) == on, r.stderr
