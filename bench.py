@@ -5,7 +5,7 @@ One step = tria_score -> tria_select -> tria_compact over the whole workload
 (every layer, sequence and KV head), inputs resident in HBM.  Prints one JSON
 line.  Default workload: Qwen3-8B-shaped, 36 layers x 8 KV heads x 32768 keys.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config qwen3_8b]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--config qwen3_8b]
 
 The default line also carries the Qwen3-32B-shaped pass under "extra_workloads"
 (--no-extra: the --config workload only).  With --read-probe GB it times the
@@ -465,8 +465,10 @@ def bench_decode(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 20; 200 with --calibrate)")
-    ap.add_argument("--warmup", type=int, default=None, help="warmup steps (default 3; 50 with --calibrate)")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; 200 with --calibrate, 20 with --decode-loop)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="warmup steps (default 100; 50 with --calibrate, 10 with --decode-loop)")
     ap.add_argument("--config", default="qwen3_8b")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--input-cache", default="", metavar="DIR",
@@ -492,11 +494,14 @@ def main() -> int:
     ap.add_argument("--select", choices=("auto", "per_group", "tiled"), default="auto",
                     help="tria_select's work distribution (auto: the library's default)")
     args = ap.parse_args()
-    # a calibration step is ~0.4 ms: more of them keep the timed region near 0.1 s
+    # The clocks ramp for tens of milliseconds after the host's set-up: a pass needs ~30
+    # warm-up steps to reach its steady rate (3 left the Qwen3-8B-shaped pass ~3 % slow).
+    # A calibration step is ~0.4 ms: more of them keep the timed region near 0.1 s.  The
+    # decode loop generates every step's rows on the host, so it runs fewer.
     if args.steps is None:
-        args.steps = 200 if args.calibrate else 20
+        args.steps = 200 if args.calibrate else (20 if args.decode_loop else 50)
     if args.warmup is None:
-        args.warmup = 50 if args.calibrate else 3
+        args.warmup = 50 if args.calibrate else (10 if args.decode_loop else 100)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the pass shards with no "
               f"exchange, so N GPUs run N independent copies of this measurement)", file=sys.stderr)
