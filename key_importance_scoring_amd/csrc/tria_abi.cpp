@@ -227,7 +227,7 @@ Layout layout(const tria_params* p, int32_t n_units, int32_t n_max) {
   L.st = off;
   off += al256(ug * sizeof(tria::SelState));
   L.tiles = off;
-  off += al256(ug * (size_t)L.n_st * 4 * 4);  // above-b1 counts, offsets, tie shares, candidates
+  off += al256(ug * (size_t)L.n_st * 3 * 4);  // above-b1 counts, offsets, candidates
   L.list = off;
   off += al256(ug * (size_t)n_max * 4);
   L.masks = off;  // per tile and thread: slots above the threshold bin, slots in it
@@ -368,7 +368,7 @@ tria_status select_impl(const tria_params* p, int32_t n_units, int32_t n_max, in
   const size_t nt = (size_t)n_units * p->n_kv_heads * L.n_st;
   tria::SelectArgs sa{n_units, n_max, b_max, p->n_kv_heads, p->sink, p->window, L.n_st, len, budget, agg,
                       reinterpret_cast<const uint32_t*>(w + L.hist), reinterpret_cast<tria::SelState*>(w + L.st),
-                      tiles, tiles + nt, tiles + 2 * nt, tiles + 3 * nt, reinterpret_cast<int32_t*>(w + L.list),
+                      tiles, tiles + nt, tiles + 2 * nt, reinterpret_cast<int32_t*>(w + L.list),
                       reinterpret_cast<tria::SelMask*>(w + L.masks),
                       reinterpret_cast<tria::SelMask*>(w + L.masks) + nt * 256, idx, cnt,
                       reinterpret_cast<int32_t*>(w)};

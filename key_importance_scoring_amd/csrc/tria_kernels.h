@@ -180,11 +180,11 @@ struct SelectArgs {
   SelState* st;               // [U][Hkv]
   int32_t* tile_gt;           // [U][Hkv][n_st] slots above b1 per tile
   int32_t* tile_off;          // [U][Hkv][n_st] output offset per tile
-  int32_t* tile_eqb;          // [U][Hkv][n_st] tied slots kept per tile
   int32_t* tile_m;            // [U][Hkv][n_st] candidates (slots of bin b1) per tile
   int32_t* list;              // [U][Hkv][n_max] candidate slots, tile j's from j * kSelTile
   SelMask* gmask;             // [U][Hkv][n_st][256] per thread: slots above b1
-  SelMask* cmask;             // [U][Hkv][n_st][256] per thread: slots of bin b1 (candidates)
+  SelMask* cmask;             // [U][Hkv][n_st][256] per thread: slots of bin b1 (candidates); k_sel_refine
+                              // then clears the bits of the candidates it drops
   int32_t* idx;               // [U][Hkv][b_max]
   int32_t* cnt;               // [U]
   int32_t* flags;

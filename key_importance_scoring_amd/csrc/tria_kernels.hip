@@ -1415,9 +1415,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 //   k_sel_refine  (per group) exact radix passes (11 + 11 + 10 bits of the
 //                 order-preserving key) over the candidates, or for at most
 //                 kSelRankMax candidates each one's rank among them, give the threshold key T
-//                 and how many slots equal to T are kept (the lowest ones); then each
-//                 tile's output offset and share of the tied slots;
-//   k_sel_emit    (per tile)  writes the tile's kept slots in ascending order.
+//                 and how many slots equal to T are kept (the lowest ones); clears
+//                 the dropped candidates from the tiles' candidate masks; then each
+//                 tile's output offset;
+//   k_sel_emit    (per tile)  writes the tile's kept slots (its masks) in ascending order.
 __device__ inline uint32_t order_key(float x) {
   const uint32_t b = __float_as_uint(x + 0.0f);  // -0 -> +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -1621,6 +1622,17 @@ __global__ __launch_bounds__(256) void k_sel_collect(SelectArgs a) {
   }
 }
 
+// Clears the candidate-mask bit of `slot` (a candidate the refinement drops).  Masks
+// narrower than 32 bits are cleared through the aligned 32-bit word that holds them
+// (the four threads' masks of one word belong to the same tile).
+__device__ inline void drop_candidate(const SelectArgs& a, int ug, int slot) {
+  constexpr int PW = 4 / (int)sizeof(SelMask);   // masks per 32-bit word
+  const int j = slot / kSelTile, local = slot - j * kSelTile;
+  const size_t e = ((size_t)ug * a.n_st + j) * 256 + local / kSelSpt;
+  uint32_t* w = reinterpret_cast<uint32_t*>(a.cmask) + e / PW;
+  atomicAnd(w, ~(1u << ((int)(e % PW) * 8 * (int)sizeof(SelMask) + local % kSelSpt)));
+}
+
 __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
   const int ug = blockIdx.x;
   const int tid = threadIdx.x;
@@ -1738,18 +1750,34 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
     T = prefix;
     keq = krem;
   }
-  // per tile: candidates above T and equal to T
+  // per tile: candidates above T and equal to T; and each candidate's fate for the
+  // emission: kept above T, or among the lowest keq slots equal to T (the list holds
+  // the candidates in slot order, so a tied candidate's rank is the number of tied
+  // ones before it in the list, counted in chunks of 512); the others are dropped
+  // from the candidate masks
+  __shared__ uint32_t s_run;   // tied candidates in the chunks before
   for (int i = tid; i < a.n_st; i += 512) {
     s_gtb[i] = 0;
     s_eqc[i] = 0;
   }
+  if (tid == 0) s_run = 0;
   __syncthreads();
   if (refine) {
-    for (int i = tid; i < m; i += 512) {
-      const int slot = cand_slot(i);
-      const uint32_t key = cand_key(i);
-      if (key > T) atomicAdd(&s_gtb[slot / kSelTile], 1);
-      else if (key == T) atomicAdd(&s_eqc[slot / kSelTile], 1);
+    for (int c0 = 0; c0 < m; c0 += 512) {
+      const int i = c0 + tid;
+      const bool in = i < m;
+      const int slot = in ? cand_slot(i) : 0;
+      const uint32_t key = in ? cand_key(i) : 0u;
+      const bool gt = in && key > T, eq = in && key == T;
+      if (gt) atomicAdd(&s_gtb[slot / kSelTile], 1);
+      else if (eq) atomicAdd(&s_eqc[slot / kSelTile], 1);
+      const uint32_t f = eq ? 1u : 0u;
+      const uint32_t incl = block_scan_incl<512>(f, wtot);
+      const uint32_t rank = s_run + incl - f;
+      if (in && !gt && !(eq && rank < keq)) drop_candidate(a, ug, slot);
+      __syncthreads();   // every thread has read s_run
+      if (tid == 511) s_run += incl;
+      __syncthreads();
     }
   }
   __syncthreads();
@@ -1778,7 +1806,6 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
     const uint32_t share = eb >= keq ? 0u : min(e, keq - eb);
     eb += e;
     a.tile_off[(size_t)ug * a.n_st + jj] = (int32_t)off;
-    a.tile_eqb[(size_t)ug * a.n_st + jj] = (int32_t)share;
     off += (uint32_t)a.tile_gt[(size_t)ug * a.n_st + jj] + (uint32_t)s_gtb[jj] + share;
   }
   if (tid == 0) {
@@ -1794,42 +1821,20 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
   const int tid = threadIdx.x;
   __shared__ uint32_t wtot[4];
-  // every load at once: the thread's masks from k_sel_collect, the group's state and
-  // the tile's offset and tie share
+  // every load at once: the thread's kept slots (above b1 from k_sel_collect, and the
+  // candidates k_sel_refine kept), the group's keep count and the tile's offset
   const int s0 = (blockIdx.x % a.n_st) * kSelTile + kSelSpt * tid;
-  uint32_t gtm = a.gmask[(size_t)blockIdx.x * 256 + tid];   // above b1: kept
-  const uint32_t cm = a.cmask[(size_t)blockIdx.x * 256 + tid];
-  const SelState st = a.st[ug];
-  const uint32_t eqb = (uint32_t)a.tile_eqb[blockIdx.x];
+  const uint32_t keep = (uint32_t)a.gmask[(size_t)blockIdx.x * 256 + tid] |
+                        (uint32_t)a.cmask[(size_t)blockIdx.x * 256 + tid];
+  const int K = a.st[ug].K;
   const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
-  const uint32_t T = (uint32_t)st.T;
-  // candidates (slots of bin b1): above the threshold key T kept, equal to T tied
-  uint32_t eqm = 0;
-  if (cm) {
-    const float* row = a.agg + (size_t)ug * a.n_max;
-    for (uint32_t m = cm; m; m &= m - 1) {
-      const int k = __ffs(m) - 1;
-      const uint32_t key = order_key(row[s0 + k]);
-      gtm |= (key > T ? 1u : 0u) << k;
-      eqm |= (key == T ? 1u : 0u) << k;
-    }
-  }
-  // tied slots of this tile are kept lowest first, up to its share eqb
-  const uint32_t ne = (uint32_t)__popc(eqm);
-  const uint32_t eq_before = block_scan_incl<256>(ne, wtot) - ne;
-  uint32_t keep = gtm;
-  uint32_t r = eq_before;
-  for (uint32_t m = eqm; m; m &= m - 1) {
-    if (r < eqb) keep |= m & (~m + 1);
-    ++r;
-  }
   const uint32_t nk = (uint32_t)__popc(keep);
   uint32_t pos = off + block_scan_incl<256>(nk, wtot) - nk;
   int32_t* out = a.idx + (size_t)ug * a.b_max;
   for (uint32_t m = keep; m; m &= m - 1) {
     // positions are < K by construction; the bound keeps a miscount from ever
     // writing past the caller's b_max row
-    if (pos < (uint32_t)st.K) out[pos] = s0 + __ffs(m) - 1;
+    if (pos < (uint32_t)K) out[pos] = s0 + __ffs(m) - 1;
     ++pos;
   }
 }
