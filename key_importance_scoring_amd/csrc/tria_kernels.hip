@@ -1413,8 +1413,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 //   k_sel_collect (per tile)  counts the tile's slots above b1 and lists its slots of
 //                 b1 in the tile's own segment of the group's candidate list;
 //   k_sel_refine  (per group) exact radix passes (11 + 11 + 10 bits of the
-//                 order-preserving key) over the candidates, or for at most
-//                 kSelRankMax candidates each one's rank among them, give the threshold key T
+//                 order-preserving key; a digit all candidates share is skipped)
+//                 over the candidates, or for at most kSelRankMax candidates each
+//                 one's rank among them, give the threshold key T
 //                 and how many slots equal to T are kept (the lowest ones); clears
 //                 the dropped candidates from the tiles' candidate masks; then each
 //                 tile's output offset;
@@ -1729,11 +1730,44 @@ __global__ __launch_bounds__(512) void k_sel_refine(SelectArgs a) {
     T = s_tk[0];
     keq = s_tk[1];
   } else if (refine) {
+    // the bits every candidate shares (AND and OR of the keys): a digit made of such
+    // bits needs no pass, since every candidate holds it and none lies above it (the
+    // candidates share a linear bin, so usually the sign, the exponent and the top of
+    // the mantissa: the whole first digit)
+    __shared__ uint32_t s_and[8], s_or[8];
+    uint32_t ka = ~0u, ko = 0u;
+    for (int i = tid; i < m; i += 512) {
+      const uint32_t key = cand_key(i);
+      ka &= key;
+      ko |= key;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      ka &= __shfl_xor(ka, o);
+      ko |= __shfl_xor(ko, o);
+    }
+    if ((tid & 63) == 0) {
+      s_and[tid >> 6] = ka;
+      s_or[tid >> 6] = ko;
+    }
+    __syncthreads();
+    ka = ~0u;
+    ko = 0u;
+    for (int w = 0; w < 8; ++w) {
+      ka &= s_and[w];
+      ko |= s_or[w];
+    }
+    const uint32_t common = ~(ka ^ ko);
     uint32_t prefix = 0, pmask = 0, krem = (uint32_t)bd.krem;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
       const int sft = pass == 0 ? 21 : (pass == 1 ? 10 : 0);   // digits of 11, 11, 10 bits
       const int nb = pass == 2 ? 1024 : 2048;
+      const uint32_t dmask = (uint32_t)(nb - 1) << sft;
+      if ((common & dmask) == dmask) {   // the same for every thread
+        prefix |= ka & dmask;
+        pmask |= dmask;
+        continue;
+      }
       for (int i = tid; i < nb; i += 512) hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < m; i += 512) {
