@@ -930,11 +930,13 @@ __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const fl
   const int c0 = max(a.sink, tile0) - tile0;
   const int c1 = min(n - a.window, tile0 + tlen) - tile0;
   // lane l reads 16-byte groups 4 (l + 64 k): all of a pass's LDS loads are
-  // independent and in flight together
+  // independent, and the unrolled loop (8 groups at 2048 keys) keeps them in flight
+  // together
   const int ngrp = (a.tile / 4 + 63) / 64;     // 16-byte groups per lane
   for (int h = wave; h < G; h += 4) {
     const float* src = s_raw + h * RS;
     float acc = 0.0f;
+#pragma unroll 8
     for (int k = 0; k < ngrp; ++k) {
       const int i = 4 * (lane + 64 * k);
       const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
@@ -948,6 +950,7 @@ __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const fl
     const double mean = cnt > 0 ? sum / cnt : 0.0;
     const float mf = (float)mean;
     float q = 0.0f;
+#pragma unroll 8
     for (int k = 0; k < ngrp; ++k) {
       const int i = 4 * (lane + 64 * k);
       const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
