@@ -893,6 +893,9 @@ __device__ inline uint64_t pack_stats(double c, double m, double m2) {
 // The end of a scored tile (lengths filled by tile_body): its per-query-head scores
 // (if wanted) and its candidate moments (count, mean, sum of squared deviations),
 // published for the other tiles of its (unit, KV head).
+// UNROLL: the moment passes' loops unrolled (the mean over offsets: faster; the
+// maximum, whose score loop has no registers to spare: slower).
+template <bool UNROLL>
 __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const float* s_raw) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -936,13 +939,18 @@ __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const fl
   for (int h = wave; h < G; h += 4) {
     const float* src = s_raw + h * RS;
     float acc = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < ngrp; ++k) {
+    auto sum_group = [&](int k) {
       const int i = 4 * (lane + 64 * k);
       const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (i + t >= c0 && i + t < c1) acc += x[t];
+    };
+    if constexpr (UNROLL) {
+#pragma unroll 8
+      for (int k = 0; k < ngrp; ++k) sum_group(k);
+    } else {
+      for (int k = 0; k < ngrp; ++k) sum_group(k);
     }
     double sum = (double)acc;
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
@@ -950,8 +958,7 @@ __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const fl
     const double mean = cnt > 0 ? sum / cnt : 0.0;
     const float mf = (float)mean;
     float q = 0.0f;
-#pragma unroll 8
-    for (int k = 0; k < ngrp; ++k) {
+    auto sq_group = [&](int k) {
       const int i = 4 * (lane + 64 * k);
       const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
 #pragma unroll
@@ -959,6 +966,12 @@ __device__ inline void tile_end(const ScoreArgs& a, const TileInfo& ti, const fl
         const float dv = x[t] - mf;
         if (i + t >= c0 && i + t < c1) q = __builtin_fmaf(dv, dv, q);
       }
+    };
+    if constexpr (UNROLL) {
+#pragma unroll 8
+      for (int k = 0; k < ngrp; ++k) sq_group(k);
+    } else {
+      for (int k = 0; k < ngrp; ++k) sq_group(k);
     }
     double m2 = (double)q;
     for (int o = 32; o > 0; o >>= 1) m2 += __shfl_xor(m2, o);
@@ -1377,7 +1390,7 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
       float* sbuf = b ? buf1 : buf0;
       tile_begin<D, P, PAGED, MAXO>(a, cur, known_len(cur), s_bt, regs);
       tile_body<D, P, PAGED, MAXO>(a, cur, sbuf, s_bt, s_bmax, &s_bug, regs);   // ends with a barrier
-      tile_end(a, cur, sbuf);
+      tile_end<!MAXO>(a, cur, sbuf);
     }
     // finalize uses the histogram region (for the maximum over offsets, the staged
     // offset blocks' region, restaged for the next tile)
