@@ -183,8 +183,10 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max)
  * Execution: the keys of each (unit, KV head) are scored in tiles of up to 2048
  * (1024 for G > 4 or the maximum over offsets; balanced in multiples of 256 when
  * n_max is larger, e.g. 1280 + 896 for 2176) by
- * concurrent workgroups that exchange their tile moments through the workspace
- * and wait (boundedly) for one another before normalising.  When a wait runs out
+ * concurrent workgroups that publish their tile moments through the workspace;
+ * the group's last tile to publish merges them once and publishes each query
+ * head's mean and deviation, which the others wait for (boundedly) before
+ * normalising.  When a wait runs out
  * (another stream's kernels holding compute units, say), the waiting workgroup
  * scores the group's keys again and forms its moments itself, and TRIA_FLAG_SYNC
  * records that this slower path ran: the results never depend on the tiles'
