@@ -1871,21 +1871,35 @@ __global__ __launch_bounds__(256) void k_sel_emit(SelectArgs a) {
   const int ug = blockIdx.x / a.n_st;
   const int tid = threadIdx.x;
   __shared__ uint32_t wtot[4];
+  __shared__ uint32_t s_cnt;
+  __shared__ int32_t s_out[kSelTile];   // the tile's kept slots, in order
   // every load at once: the thread's kept slots (above b1 from k_sel_collect, and the
-  // candidates k_sel_refine kept), the group's keep count and the tile's offset
+  // candidates k_sel_refine kept), the group's counts and the tile's offset
   const int s0 = (blockIdx.x % a.n_st) * kSelTile + kSelSpt * tid;
   const uint32_t keep = (uint32_t)a.gmask[(size_t)blockIdx.x * 256 + tid] |
                         (uint32_t)a.cmask[(size_t)blockIdx.x * 256 + tid];
-  const int K = a.st[ug].K;
+  const SelState st = a.st[ug];
+  const uint32_t K = (uint32_t)st.K;
   const uint32_t off = (uint32_t)a.tile_off[blockIdx.x];
   const uint32_t nk = (uint32_t)__popc(keep);
-  uint32_t pos = off + block_scan_incl<256>(nk, wtot) - nk;
-  int32_t* out = a.idx + (size_t)ug * a.b_max;
-  for (uint32_t m = keep; m; m &= m - 1) {
-    // positions are < K by construction; the bound keeps a miscount from ever
-    // writing past the caller's b_max row
-    if (pos < (uint32_t)K) out[pos] = s0 + __ffs(m) - 1;
-    ++pos;
+  const uint32_t incl = block_scan_incl<256>(nk, wtot);
+  uint32_t pos = incl - nk;
+  int32_t* out = a.idx + (size_t)ug * a.b_max + off;
+  // The run's places are < K by construction; the bounds keep a miscount from ever
+  // writing past the caller's b_max row.  Where more than one slot in eight is kept,
+  // the run goes through LDS and out with coalesced stores (each thread's own
+  // stores would spread over many lines); sparser runs are written directly.
+  if ((int64_t)st.K * 8 > (int64_t)st.n) {   // the same for the whole workgroup
+    for (uint32_t m = keep; m; m &= m - 1) s_out[pos++] = s0 + __ffs(m) - 1;
+    if (tid == 255) s_cnt = incl;
+    __syncthreads();
+    const uint32_t lim = off < K ? min(s_cnt, K - off) : 0u;
+    for (uint32_t i = tid; i < lim; i += 256) out[i] = s_out[i];
+  } else {
+    for (uint32_t m = keep; m; m &= m - 1) {
+      if (off + pos < K) out[pos] = s0 + __ffs(m) - 1;
+      ++pos;
+    }
   }
 }
 
