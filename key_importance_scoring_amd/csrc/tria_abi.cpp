@@ -271,32 +271,54 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
     return fail(TRIA_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if (n_units == 0 || n_max == 0) return TRIA_OK;
   const int omax = p->offset_reduce == TRIA_OFFSETS_MAX ? 1 : 0;
-  if (omax && tria::score_lds(p->head_dim, p->group, k->block_table != nullptr, 1, L.ob.nblk, L.tile,
-                             k->block_size) > 160 * 1024)
+  const bool paged = k->block_table != nullptr;
+  if (omax && tria::score_lds(p->head_dim, p->group, paged, 1, L.ob.nblk, L.tile, k->block_size, 0) > 160 * 1024)
     return fail(TRIA_ESHAPE, "maximum over %d offsets: %d coefficient blocks of head_dim %d do not fit in LDS",
                 p->n_offsets, L.ob.nblk, p->head_dim);
-  // the tiles of one (unit, KV head) wait for each other: they must all fit at once
-  const int cap = tria::score_capacity(p->head_dim, p->pairing, k->block_table != nullptr, p->group, omax,
-                                       L.ob.nblk, L.tile, k->block_size);
-  if (cap < 0) return fail(TRIA_ELAUNCH, "k_score occupancy query failed");
-  if (L.n_tiles > cap)
-    return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the device holds %d",
-                n_max, L.n_tiles, cap);
   const int wg_cap = g_score_wg_cap.load();
-  if (wg_cap > 0 && L.n_tiles > wg_cap)
+  // The mean over offsets with G > 4 keeps two score buffers of 1024-key tiles; for a
+  // dense cache, when
+  // every tile of the call fits on the device at once with one buffer of twice as
+  // long tiles, that mode runs instead: no tile waits on another round, and half as
+  // many tiles pay the per-tile exchange (e.g. 8 KV heads x 131072 keys, G = 8: one
+  // round of 512 tiles instead of two of 512).  The choice depends on the device's
+  // resident capacity only, not on tria_score_max_workgroups: the tiles, and so the
+  // rounding of the merged moments, do not change with the grid (a capped grid runs
+  // the single-buffer mode in several rounds; its waits still end, since a workgroup
+  // waits only once its own tile is published)
+  int tile = L.tile, n_tiles = L.n_tiles, single = 0;
+  if (!omax && !paged && p->group > 4) {
+    const int t1 = tria::single_tile_keys(n_max);
+    const int nt1 = (n_max + t1 - 1) / t1;
+    const int cap1 =
+        tria::score_capacity(p->head_dim, p->pairing, paged, p->group, 0, L.ob.nblk, t1, k->block_size, 1);
+    if (cap1 > 0 && (long)n_units * p->n_kv_heads * nt1 <= (long)cap1) {
+      tile = t1;
+      n_tiles = nt1;
+      single = 1;
+    }
+  }
+  // the tiles of one (unit, KV head) wait for each other: they must all fit at once
+  const int cap = tria::score_capacity(p->head_dim, p->pairing, paged, p->group, omax, L.ob.nblk, tile,
+                                       k->block_size, single);
+  if (cap < 0) return fail(TRIA_ELAUNCH, "k_score occupancy query failed");
+  if (n_tiles > cap)
+    return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the device holds %d",
+                n_max, n_tiles, cap);
+  if (wg_cap > 0 && n_tiles > wg_cap)
     return fail(TRIA_ESHAPE, "n_max %d needs %d concurrent score tiles per (unit, KV head); the workgroup cap is %d",
-                n_max, L.n_tiles, wg_cap);
+                n_max, n_tiles, wg_cap);
   if (log_on()) {
-    const long tiles = (long)n_units * p->n_kv_heads * L.n_tiles;
+    const long tiles = (long)n_units * p->n_kv_heads * n_tiles;
     const int grid_cap = wg_cap > 0 && wg_cap < cap ? wg_cap : cap;
     tlog("score: %d units x %d KV heads x n_max %d, d %d, G %d, %s, %s K, %d offsets (%s), %s aggregation: "
-         "%s, tiles of %d keys (%d per (unit, KV head), %ld in all), grid %ld (resident capacity %d, cap %d), "
+         "%s, tiles of %d keys (%d per (unit, KV head), %ld in all), %s, grid %ld (resident capacity %d, cap %d), "
          "LDS %zu B, moment wait %d polls, workspace %zu of %zu B",
          n_units, p->n_kv_heads, n_max, p->head_dim, p->group, pairing_name(p->pairing), layout_name(k),
          p->n_offsets, omax ? "maximum" : "mean", p->agg == TRIA_AGG_MAX ? "max" : "mean",
-         omax ? "k_score_max" : "k_score", L.tile, L.n_tiles, tiles, tiles < grid_cap ? tiles : (long)grid_cap, cap,
-         wg_cap, tria::score_lds(p->head_dim, p->group, k->block_table != nullptr, omax, L.ob.nblk, L.tile,
-                                 k->block_size),
+         omax ? "k_score_max" : "k_score", tile, n_tiles, tiles, single ? "one score buffer" : "two score buffers",
+         tiles < grid_cap ? tiles : (long)grid_cap, cap, wg_cap,
+         tria::score_lds(p->head_dim, p->group, paged, omax, L.ob.nblk, tile, k->block_size, single),
          g_wait_polls.load(), L.total, ws_bytes);
   }
   if (dry) return TRIA_OK;
@@ -316,7 +338,7 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
   float* nconst = reinterpret_cast<float*>(w + L.nconst);
   tria::CoefArgs ca{kview(k), n_units, p->n_kv_heads * p->group, p->n_kv_heads, p->head_dim, p->n_layers,
                     p->pairing, std::log(p->rope_base), len, unit_layer, q_pos, q_mean_re, q_mean_im, q_abs_mean,
-                    p->group, L.n_tiles, L.tile, n_max, B, nconst,
+                    p->group, n_tiles, tile, n_max, B, nconst,
                     reinterpret_cast<uint64_t*>(part), next_tile, hist, flags, omax,
                     reinterpret_cast<uint32_t*>(w + L.Bmax), L.ob, reinterpret_cast<uint64_t*>(w + L.gstat),
                     reinterpret_cast<int32_t*>(w + L.arrive)};
@@ -324,10 +346,10 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
   if ((st = launch_status(e, "k_coef")) != TRIA_OK) return st;
 
   tria::ScoreArgs sa{kview(k), n_units, n_max, p->n_kv_heads, p->group, p->sink, p->window,
-                     L.tile, L.n_tiles, p->agg,
+                     tile, n_tiles, p->agg,
                      len, B, nconst, raw, part, agg, next_tile, hist, flags, omax,
                      reinterpret_cast<const uint32_t*>(w + L.Bmax), L.ob, g_wait_polls.load(),
-                     reinterpret_cast<uint64_t*>(w + L.gstat), reinterpret_cast<int32_t*>(w + L.arrive)};
+                     reinterpret_cast<uint64_t*>(w + L.gstat), reinterpret_cast<int32_t*>(w + L.arrive), single};
   e = timed(kIdScore, s, [&] { return tria::launch_score(sa, p->head_dim, p->pairing, wg_cap, s); });
   return launch_status(e, "k_score");
 }

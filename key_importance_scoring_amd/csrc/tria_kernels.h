@@ -28,13 +28,20 @@ constexpr int kScoreTileMax = 2048;
 // live in LDS), balanced in multiples of 256 (each wave takes a quarter of a tile
 // in 64-key stages), so that a row just past a multiple of the cap is not followed
 // by a nearly empty tile.
-inline int score_tile_keys(int group, int omax, int n_max) {
-  const int cap = group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : TRIA_SCORE_TILE_LARGE_G;
+inline int balanced_tile_keys(int cap, int n_max) {
   if (n_max <= cap) return cap;
   const int nt = (n_max + cap - 1) / cap;
   const int t = ((n_max + nt - 1) / nt + 255) / 256 * 256;
   return t < cap ? t : cap;
 }
+inline int score_tile_keys(int group, int omax, int n_max) {
+  return balanced_tile_keys(group <= 4 && !omax ? TRIA_SCORE_TILE_SMALL_G : TRIA_SCORE_TILE_LARGE_G, n_max);
+}
+// With one score buffer a workgroup (dense caches, the mean over offsets, G > 4) takes tiles of
+// this many keys; tria_score picks that mode when every tile of the call fits on
+// the device at once.  The workspace is sized for score_tile_keys' smaller tiles,
+// whose tile count bounds this one's.
+inline int single_tile_keys(int n_max) { return balanced_tile_keys(TRIA_SCORE_TILE_SMALL_G, n_max); }
 // A tile's published moments start as this bit pattern (cleared by k_coef): a NaN
 // whose low payload bits are set, which no moment computed from fp32 scores can
 // take (NaNs that arithmetic produces keep an fp32 payload or are the default one).
@@ -139,6 +146,7 @@ struct ScoreArgs {
   int32_t wait_polls;         // polls of a finalisation's wait (< 0: compute the moments directly at once)
   uint64_t* gstat;            // [U][Hq] merged (mean, 1 / deviation) per query head: two fp32 in one word
   int32_t* arrive;            // [U][Hkv] non-empty tiles that have published their moments
+  int32_t single;             // 1: one LDS score buffer, each tile finalised as soon as it is scored
 };
 
 // Per-(unit, KV head) state of the selection, in the workspace.
@@ -226,9 +234,10 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s);
 // Workgroups of k_score that fit on the device at once (-1 on error).  Every tile
 // of one (unit, KV head) must be resident together for the moment exchange.
-int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size,
+                   int single);
 // LDS bytes of one k_score workgroup for tiles of `tile` keys (block_size: of a paged cache)
-size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int block_size);
+size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int block_size, int single);
 // strategy: 0 automatic, 1 per group (when n_max fits), 2 tiled
 hipError_t launch_select(const SelectArgs& a, int strategy, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);

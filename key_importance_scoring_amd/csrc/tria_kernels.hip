@@ -1289,7 +1289,10 @@ __host__ __device__ inline int score_scratch(bool omax, bool paged, int tile, in
 // order from a counter.  Each workgroup scores and publishes its current tile, and
 // only then finalises its previous one (two LDS score buffers): by that time the
 // previous tile's group has nearly always published, so the moment exchange hides
-// behind the streaming.  With at most kListUnits units every workgroup first reads
+// behind the streaming.  In the single-buffer mode (a.single; dense caches and the
+// mean over offsets: every tile of the call resident at once, with tiles twice as
+// long as two buffers would allow) each tile is finalised right after it is
+// published; a workgroup then waits holding no unpublished tile.  With at most kListUnits units every workgroup first reads
 // all lengths into LDS, and the claims run over the tiles that hold keys only (the
 // tiles of a (unit, KV head) still consecutive); k_coef has published empty tiles'
 // moments as zeros.  A workgroup waits only on tiles that are already
@@ -1309,18 +1312,19 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
   __shared__ int s_bug;   // maximum over offsets: the (unit, KV head) whose offset blocks are staged
   const int G = a.group;
   const int RS = a.tile + 16;
+  const int nbuf = !PAGED && !MAXO && a.single ? 1 : 2;
   float* buf0 = s_dyn;
-  float* buf1 = s_dyn + G * RS;
+  float* buf1 = s_dyn + (nbuf - 1) * G * RS;
   // LDS after the two score buffers: one region for the tile's block ids (paged)
   // and the finalisation's histogram (they are never live together; the maximum over
   // offsets keeps the histogram in the staged offset blocks' region instead, restaged
   // after every finalisation), the units' lengths and tile prefix, the staged offset
   // blocks (the maximum over offsets)
   const int scratch = score_scratch(MAXO, PAGED, a.tile, a.k.bs);
-  int* s_bt = reinterpret_cast<int*>(s_dyn + 2 * G * RS);
+  int* s_bt = reinterpret_cast<int*>(s_dyn + nbuf * G * RS);
   int* s_len = s_bt + scratch;            // [kListUnits] lengths
   int* s_pre = s_len + kListUnits;        // [kListUnits + 1] tiles of the units before
-  const int used = 2 * G * RS + scratch + 2 * kListUnits + 1;
+  const int used = nbuf * G * RS + scratch + 2 * kListUnits + 1;
   u32x4* s_bmax = reinterpret_cast<u32x4*>(s_dyn + ((used + 3) & ~3));   // 16-byte aligned
   uint32_t* s_hist = MAXO ? reinterpret_cast<uint32_t*>(s_bmax) : reinterpret_cast<uint32_t*>(s_bt);
   if (threadIdx.x == 0) s_bug = -1;
@@ -1391,6 +1395,14 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
       tile_begin<D, P, PAGED, MAXO>(a, cur, known_len(cur), s_bt, regs);
       tile_body<D, P, PAGED, MAXO>(a, cur, sbuf, s_bt, s_bmax, &s_bug, regs);   // ends with a barrier
       tile_end<!MAXO>(a, cur, sbuf);
+      if constexpr (!PAGED && !MAXO) {
+        if (a.single) {
+          // one score buffer: the tile is finalised at once (its buffer is rewritten
+          // only after the barrier of the next claim)
+          finalize_tile<D, P, PAGED, MAXO>(a, cur, known_len(cur), sbuf, s_hist);
+          continue;
+        }
+      }
     }
     // finalize uses the histogram region (for the maximum over offsets, the staged
     // offset blocks' region, restaged for the next tile)
@@ -2443,20 +2455,22 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int block_size) {
-  // two score buffers, the region shared by the tile's block ids and (the mean) the
-  // finalisation's histogram, the units' lengths and tile prefix, and for the maximum
-  // over offsets the staged offset blocks, whose region also holds the histogram
-  const size_t used = (size_t)2 * group * (tile + 16) + (size_t)score_scratch(omax, paged, tile, block_size) +
-                      (size_t)(2 * kListUnits + 1);
+size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int block_size, int single) {
+  // two score buffers (one in the single-buffer mode), the region shared by the
+  // tile's block ids and (the mean) the finalisation's histogram, the units' lengths
+  // and tile prefix, and for the maximum over offsets the staged offset blocks, whose
+  // region also holds the histogram
+  const size_t used = (size_t)(single ? 1 : 2) * group * (tile + 16) +
+                      (size_t)score_scratch(omax, paged, tile, block_size) + (size_t)(2 * kListUnits + 1);
   if (!omax) return used * 4;
   // the blocks, then the lanes' reference magnitudes (d/64 16-byte operands a lane)
   const size_t blocks = (size_t)nblk * (d / 32) * 64 * 16 + (size_t)(d / 64) * 64 * 16;
   return ((used + 3) & ~(size_t)3) * 4 + (blocks > (size_t)kBins * 4 ? blocks : (size_t)kBins * 4);
 }
 
-int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size) {
-  const size_t lds = score_lds(d, group, paged, omax, nblk, tile, block_size);
+int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size,
+                   int single) {
+  const size_t lds = score_lds(d, group, paged, omax, nblk, tile, block_size, single);
   int per_cu = 0, dev = 0, cus = 0;
   hipError_t e = hipErrorInvalidValue;
 #define TRIA_OCC_CASE(DD, PP, PG, MX)                                                                     \
@@ -2490,11 +2504,11 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
   const long tiles = (long)a.n_units * a.hkv * a.n_tiles;
   if (tiles == 0) return hipSuccess;
   const bool paged = a.k.bt != nullptr;
-  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk, a.tile, a.k.bs);
+  int cap = score_capacity(d, pairing, paged, a.group, a.omax, a.ob.nblk, a.tile, a.k.bs, a.single);
   if (max_wg > 0 && max_wg < cap) cap = max_wg;
   if (cap < a.n_tiles) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
-  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk, a.tile, a.k.bs);
+  const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk, a.tile, a.k.bs, a.single);
 #define TRIA_SCORE_CASE(DD, PP, PG, MX)                                       \
   if (d == DD && pairing == PP && paged == PG && (a.omax != 0) == MX) {      \
     if (MX) hipLaunchKernelGGL((k_score_max<DD, PP, PG>), grid, blk, lds, s, a); \

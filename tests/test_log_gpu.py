@@ -56,3 +56,21 @@ def test_log_per_group_selection_and_paged_views(capfd):
     assert any(l.startswith("[tria] score:") and "paged K" in l for l in lines), lines
     assert any(l.startswith("[tria] select:") and "k_sel_group" in l for l in lines), lines
     assert any(l.startswith("[tria] compact:") and "paged -> paged" in l for l in lines), lines
+
+
+def test_log_score_buffer_mode(capfd):
+    # G = 8, the mean over offsets: a call whose 2048-key tiles all fit on the device
+    # at once takes the single-buffer mode (8 KV heads x 3 tiles); Qwen3-8B's G = 4
+    # keeps two buffers
+    cfg = synth.CONFIGS["long_context"].replace(name="log_single", n_kv=6000, budget=600)
+    print(f"[log] {cfg.name}", flush=True)
+    prob = DeviceProblem(cfg)
+    lines = _run_logged(prob, capfd)
+    assert prob.flags() == 0
+    score = [l for l in lines if l.startswith("[tria] score:")]
+    assert len(score) == 1, lines
+    assert "tiles of 2048 keys (3 per (unit, KV head), 24 in all), one score buffer" in score[0], score
+    cfg = synth.CONFIGS["qwen3_8b"].replace(name="log_two", n_layers=1, n_kv=3000, budget=600)
+    prob = DeviceProblem(cfg)
+    lines = _run_logged(prob, capfd)
+    assert any(l.startswith("[tria] score:") and "two score buffers" in l for l in lines), lines
