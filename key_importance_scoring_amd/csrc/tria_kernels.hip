@@ -1200,6 +1200,10 @@ __device__ inline void finalize_tile(const ScoreArgs& a, TileInfo ti, int n_know
   __shared__ float s_mean[kMaxGroup], s_inv[kMaxGroup];
   __shared__ int s_direct;   // a head's wait ran out: the group's moments are computed directly
   tile_len(a, ti, n_known >= 0 ? n_known : a.len[ti.u], false);
+  // an empty tile (past its unit's length: claimed only when the units are not
+  // listed) has no aggregates and no histogram counts, and must not wait: in a unit
+  // of length 0 no tile publishes the group's moments
+  if (ti.tlen == 0) return;
   if (threadIdx.x == 0) s_direct = a.wait_polls < 0;
   __syncthreads();
 

@@ -268,6 +268,30 @@ def test_empty_and_zero_budget_units(strategy):
         check_unit(prob, unit)
 
 
+def test_many_units_with_empty_ones():
+    """More units than the score kernel lists (520 > 512): every tile is claimed, also
+    the empty ones past a unit's length.  Units of length 0 have no tile that would
+    publish their moments; their tiles must finish without waiting (no expired wait,
+    so no TRIA_FLAG_SYNC) and leave the other units' results as the oracle's."""
+    cfg = C["batched_decode"].replace(name="many_units", n_seqs=520, n_kv=300, ragged_min=100, window=16)
+    log(f"[parity] {cfg.name}: {cfg.n_units} units, every 37th emptied")
+    prob = DeviceProblem(cfg)
+    empty = list(range(5, cfg.n_units, 37))
+    for unit in empty:
+        prob.len[unit] = 0
+    prob.run()
+    torch.cuda.synchronize()
+    prob.check_guards()
+    assert prob.flags() == 0
+    cnt = prob.cnt.cpu().numpy()
+    assert all(cnt[unit] == 0 for unit in empty)
+    kept = {}
+    for unit in (0, 4, 6, 41, 43, 519):
+        assert unit not in empty
+        kept[unit] = check_unit(prob, unit)
+    _check_oracle_compaction(prob, kept)
+
+
 def test_device_flags_record_bad_metadata(strategy):
     """Out-of-contract device metadata is clamped by the kernels and reported."""
     cfg = C["batched_decode"].replace(name="flags", n_seqs=3, n_kv=500, ragged_min=200)
