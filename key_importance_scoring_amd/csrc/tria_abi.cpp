@@ -316,7 +316,8 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
          "LDS %zu B, moment wait %d polls, workspace %zu of %zu B",
          n_units, p->n_kv_heads, n_max, p->head_dim, p->group, pairing_name(p->pairing), layout_name(k),
          p->n_offsets, omax ? "maximum" : "mean", p->agg == TRIA_AGG_MAX ? "max" : "mean",
-         omax ? "k_score_max" : "k_score", tile, n_tiles, tiles, single ? "one score buffer" : "two score buffers",
+         omax ? "k_score_max" : single ? "k_score_single" : "k_score", tile, n_tiles, tiles,
+         single ? "one score buffer" : "two score buffers",
          tiles < grid_cap ? tiles : (long)grid_cap, cap, wg_cap,
          tria::score_lds(p->head_dim, p->group, paged, omax, L.ob.nblk, tile, k->block_size, single),
          g_wait_polls.load(), L.total, ws_bytes);

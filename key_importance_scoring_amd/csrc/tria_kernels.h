@@ -146,7 +146,7 @@ struct ScoreArgs {
   int32_t wait_polls;         // polls of a finalisation's wait (< 0: compute the moments directly at once)
   uint64_t* gstat;            // [U][Hq] merged (mean, 1 / deviation) per query head: two fp32 in one word
   int32_t* arrive;            // [U][Hkv] non-empty tiles that have published their moments
-  int32_t single;             // 1: one LDS score buffer, each tile finalised as soon as it is scored
+  int32_t single;             // 1: k_score_single (one LDS score buffer, each tile finalised as soon as it is scored)
 };
 
 // Per-(unit, KV head) state of the selection, in the workspace.

@@ -1293,10 +1293,10 @@ __host__ __device__ inline int score_scratch(bool omax, bool paged, int tile, in
 // order from a counter.  Each workgroup scores and publishes its current tile, and
 // only then finalises its previous one (two LDS score buffers): by that time the
 // previous tile's group has nearly always published, so the moment exchange hides
-// behind the streaming.  In the single-buffer mode (a.single; dense caches and the
-// mean over offsets: every tile of the call resident at once, with tiles twice as
-// long as two buffers would allow) each tile is finalised right after it is
-// published; a workgroup then waits holding no unpublished tile.  With at most kListUnits units every workgroup first reads
+// behind the streaming.  In the single-buffer mode (SINGLE, k_score_single; dense
+// caches and the mean over offsets: every tile of the call resident at once, with
+// tiles twice as long as two buffers would allow) each tile is finalised right after
+// it is published; a workgroup then waits holding no unpublished tile.  With at most kListUnits units every workgroup first reads
 // all lengths into LDS, and the claims run over the tiles that hold keys only (the
 // tiles of a (unit, KV head) still consecutive); k_coef has published empty tiles'
 // moments as zeros.  A workgroup waits only on tiles that are already
@@ -1309,14 +1309,15 @@ __host__ __device__ inline int score_scratch(bool omax, bool paged, int tile, in
 // the previous tile's finalisation, and two other key layouts over the waves: none
 // changed the score kernel's time on the Qwen3-8B-shaped cache by more than 2 %, the
 // first made it 2 % slower.)
-template <int D, int P, bool PAGED, bool MAXO>
+template <int D, int P, bool PAGED, bool MAXO, bool SINGLE = false>
 __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
+  static_assert(!SINGLE || (!PAGED && !MAXO), "the single-buffer mode: dense caches, the mean over offsets");
   extern __shared__ float s_dyn[];
   __shared__ int s_t;
   __shared__ int s_bug;   // maximum over offsets: the (unit, KV head) whose offset blocks are staged
   const int G = a.group;
   const int RS = a.tile + 16;
-  const int nbuf = !PAGED && !MAXO && a.single ? 1 : 2;
+  constexpr int nbuf = SINGLE ? 1 : 2;
   float* buf0 = s_dyn;
   float* buf1 = s_dyn + (nbuf - 1) * G * RS;
   // LDS after the two score buffers: one region for the tile's block ids (paged)
@@ -1399,13 +1400,11 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
       tile_begin<D, P, PAGED, MAXO>(a, cur, known_len(cur), s_bt, regs);
       tile_body<D, P, PAGED, MAXO>(a, cur, sbuf, s_bt, s_bmax, &s_bug, regs);   // ends with a barrier
       tile_end<!MAXO>(a, cur, sbuf);
-      if constexpr (!PAGED && !MAXO) {
-        if (a.single) {
-          // one score buffer: the tile is finalised at once (its buffer is rewritten
-          // only after the barrier of the next claim)
-          finalize_tile<D, P, PAGED, MAXO>(a, cur, known_len(cur), sbuf, s_hist);
-          continue;
-        }
+      if constexpr (SINGLE) {
+        // one score buffer: the tile is finalised at once (its buffer is rewritten
+        // only after the barrier of the next claim)
+        finalize_tile<D, P, PAGED, MAXO>(a, cur, known_len(cur), sbuf, s_hist);
+        continue;
       }
     }
     // finalize uses the histogram region (for the maximum over offsets, the staged
@@ -1424,6 +1423,12 @@ __device__ __forceinline__ void score_kernel(const ScoreArgs& a) {
 template <int D, int P, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score(ScoreArgs a) {
   score_kernel<D, P, PAGED, false>(a);
+}
+
+// The single-buffer mode of the mean over offsets (dense caches; see score_kernel).
+template <int D, int P>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_score_single(ScoreArgs a) {
+  score_kernel<D, P, false, false, true>(a);
 }
 
 // The maximum over offsets: two workgroups per CU when LDS allows (G <= 4), so at
@@ -2480,7 +2485,10 @@ int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk
 #define TRIA_OCC_CASE(DD, PP, PG, MX)                                                                     \
   if (d == DD && pairing == PP && paged == PG && (omax != 0) == MX)                                       \
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(                                                     \
-        &per_cu, MX ? (const void*)k_score_max<DD, PP, PG> : (const void*)k_score<DD, PP, PG>, 256, lds);
+        &per_cu,                                                                                          \
+        MX ? (const void*)k_score_max<DD, PP, PG>                                                        \
+           : (!PG && single ? (const void*)k_score_single<DD, PP> : (const void*)k_score<DD, PP, PG>),   \
+        256, lds);
 #define TRIA_OCC_CASES(MX)        \
   TRIA_OCC_CASE(64, 0, false, MX)  \
   TRIA_OCC_CASE(64, 1, false, MX)  \
@@ -2513,11 +2521,12 @@ hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipS
   if (cap < a.n_tiles) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), blk(256);
   const size_t lds = score_lds(d, a.group, paged, a.omax, a.ob.nblk, a.tile, a.k.bs, a.single);
-#define TRIA_SCORE_CASE(DD, PP, PG, MX)                                       \
-  if (d == DD && pairing == PP && paged == PG && (a.omax != 0) == MX) {      \
-    if (MX) hipLaunchKernelGGL((k_score_max<DD, PP, PG>), grid, blk, lds, s, a); \
-    else hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, lds, s, a);   \
-    return hipGetLastError();                                                 \
+#define TRIA_SCORE_CASE(DD, PP, PG, MX)                                                  \
+  if (d == DD && pairing == PP && paged == PG && (a.omax != 0) == MX) {                 \
+    if (MX) hipLaunchKernelGGL((k_score_max<DD, PP, PG>), grid, blk, lds, s, a);        \
+    else if (!PG && a.single) hipLaunchKernelGGL((k_score_single<DD, PP>), grid, blk, lds, s, a); \
+    else hipLaunchKernelGGL((k_score<DD, PP, PG>), grid, blk, lds, s, a);              \
+    return hipGetLastError();                                                            \
   }
 #define TRIA_SCORE_CASES(MX)        \
   TRIA_SCORE_CASE(64, 0, false, MX)  \
