@@ -181,8 +181,9 @@ size_t tria_workspace_size(const tria_params* p, int32_t n_units, int32_t n_max)
  *               are left untouched
  *   ws          [device] workspace of ws_bytes >= tria_workspace_size(...)
  * Execution: the keys of each (unit, KV head) are scored in tiles of up to 2048
- * (1024 for G > 4 or the maximum over offsets; balanced in multiples of 256 when
- * n_max is larger, e.g. 1280 + 896 for 2176) by
+ * (1024 for G > 4 or the maximum over offsets, except for a dense cache with the
+ * mean over offsets whose 2048-key tiles all fit on the device at once; balanced
+ * in multiples of 256 when n_max is larger, e.g. 1280 + 896 for 2176) by
  * concurrent workgroups that publish their tile moments through the workspace;
  * the group's last tile to publish merges them once and publishes each query
  * head's mean and deviation, which the others wait for (boundedly) before
