@@ -276,16 +276,16 @@ tria_status score_impl(const tria_params* p, const tria_kv_view* k, int32_t n_un
     return fail(TRIA_ESHAPE, "maximum over %d offsets: %d coefficient blocks of head_dim %d do not fit in LDS",
                 p->n_offsets, L.ob.nblk, p->head_dim);
   const int wg_cap = g_score_wg_cap.load();
-  // The mean over offsets with G > 4 keeps two score buffers of 1024-key tiles; for a
-  // dense cache, when
-  // every tile of the call fits on the device at once with one buffer of twice as
-  // long tiles, that mode runs instead: no tile waits on another round, and half as
-  // many tiles pay the per-tile exchange (e.g. 8 KV heads x 131072 keys, G = 8: one
-  // round of 512 tiles instead of two of 512).  The choice depends on the device's
-  // resident capacity only, not on tria_score_max_workgroups: the tiles, and so the
-  // rounding of the merged moments, do not change with the grid (a capped grid runs
-  // the single-buffer mode in several rounds; its waits still end, since a workgroup
-  // waits only once its own tile is published)
+  // The mean over offsets with G > 4 keeps two score buffers of 1024-key tiles; for
+  // a dense cache whose tiles all fit on the device at once with one buffer of twice
+  // as long tiles, that mode (k_score_single) runs instead: no tile waits on another
+  // round, and half as many tiles pay the per-tile exchange (e.g. 8 KV heads x
+  // 131072 keys, G = 8: one round of 512 tiles instead of two of 512).  The choice
+  // depends on the device's resident capacity only, not on
+  // tria_score_max_workgroups: the tiles, and so the rounding of the merged moments,
+  // do not change with the grid (a capped grid runs the single-buffer mode in
+  // several rounds; its waits still end, since a workgroup waits only once its own
+  // tile is published)
   int tile = L.tile, n_tiles = L.n_tiles, single = 0;
   if (!omax && !paged && p->group > 4) {
     const int t1 = tria::single_tile_keys(n_max);
