@@ -2,7 +2,8 @@
 allocation, memset or synchronisation, so a caller can capture them once and replay
 them.  Every replay, with the program's own eager work and synchronisations between
 replays, must give bit-identical aggregates, kept slots, counts and compacted rows to
-the eager calls (the maximum over offsets and a paged cache included).
+the eager calls (the maximum over offsets, a paged cache and the single-buffer score
+kernel included).
 """
 import pytest
 import torch
@@ -20,6 +21,8 @@ CASES = {
     "q8_mean": C["qwen3_8b"].replace(name="graph_q8", n_layers=2, n_kv=5003, budget=1000),
     "bd_paged_max": C["batched_decode"].replace(name="graph_bd", n_seqs=5, n_kv=3000, ragged_min=500,
                                                 offset_reduce="max"),
+    # G = 8, dense: the single-buffer score kernel
+    "lc_single": C["long_context"].replace(name="graph_lc", n_kv=6000, budget=600),
 }
 
 
