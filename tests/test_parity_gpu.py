@@ -35,6 +35,10 @@ SMALL = {
                                             budget=900),
     "d64_inter": C["tiny"].replace(name="d64_inter", pairing="interleaved", n_kv=3001, budget=1200, sink=3,
                                    agg="max"),
+    # G > 4 on a dense cache at d = 256 and d = 64: the single-buffer score kernel
+    "d256_g8": C["long_context"].replace(name="d256_g8", head_dim=256, n_kv_heads=2, n_kv=4500, budget=900,
+                                         pairing="neox"),
+    "d64_g6": C["tiny"].replace(name="d64_g6", group=6, n_kv=3333, budget=1100, agg="mean"),
     "g1_g7": C["qwen3_8b"].replace(name="g1", n_layers=1, n_kv_heads=3, group=1, n_kv=2300, budget=400),
     "g7": C["qwen3_8b"].replace(name="g7", n_layers=1, n_kv_heads=2, group=7, n_kv=2222, budget=800, agg="mean"),
     "keep_all": C["tiny"].replace(name="keep_all", n_kv=900, budget=5000),
