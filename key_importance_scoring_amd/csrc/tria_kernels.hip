@@ -186,9 +186,13 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   __shared__ float s_ref[F];            // reference magnitudes (bf16 values)
   __shared__ float s_rsum[256];
 
-  // blockIdx.z > 0 (the maximum over offsets only) writes a share of the offset
-  // blocks' operands and nothing else
+  // blockIdx.z > 0: with the maximum over offsets, a block that writes a share of
+  // the offset blocks' operands and nothing else; with the mean over offsets and few
+  // (unit, KV head) pairs, one block per query head hz, each forming and writing
+  // that head's coefficients, norm weights and shift (block 0 also the rest)
   const bool first = blockIdx.z == 0;
+  const int hz = !a.omax && gridDim.z > 1 ? (int)blockIdx.z : -1;
+  const bool own_b = first || hz >= 0;   // writes B operands (its head's, or all heads')
   const int n_u = clamp_len(a.len, u, a.n_max, nullptr);
   // Reference magnitudes of the norm term: r_f = the mean |k_f| over kRefRows slots
   // spread over the unit's keys.  The score kernel forms sum_f n_f (|k_f| - r_f) and
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       ref_re[i] = ref_im[i] = 0u;
-      if (first && n_u > 0) {
+      if (own_b && n_u > 0) {
         const int r = sub + subs * i;
         const int slot = (int)(((2 * (int64_t)r + 1) * n_u) / (2 * kRefRows));
         const uint16_t* row = row_ptr(a.k, u, g, slot, nullptr);
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   for (int k = 0; k < PER; ++k) {
     const int p = t + 256 * k, h = p / F, b = p % F;
     mr[k] = mi[k] = ab[k] = 0.0;
-    if (ok && h < G) {
+    if (ok && h < G && (hz < 0 || h == hz)) {
       const size_t si = ((size_t)layer * hq + g * G + h) * F + b;
       mr[k] = a.q_re[si];
       mi[k] = a.q_im[si];
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int p = t + 256 * k, h = p / F, b = p % F;
-    if (h >= G) continue;
+    if (h >= G || (hz >= 0 && h != hz)) continue;
     // c = mu' e^{i w q_pos} with mu' = E[q_f] W_f  [Fold note, Eq. 7]
     const double cr = mr[k] * rot_re[b] - mi[k] * rot_im[b];
     const double ci = mr[k] * rot_im[b] + mi[k] * rot_re[b];
@@ -313,9 +317,10 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   }
   __syncthreads();
   // the constant each query head's norm term was shifted by: sum_f n_f r_f (fp64)
-  if (first) {
+  if (own_b) {
     const int lane = t & 63, wave = t >> 6;
     for (int h = wave; h < G; h += 4) {
+      if (hz >= 0 && h != hz) continue;
       double c = 0.0;
       for (int f = lane; f < F; f += 64) c += (double)s_n[h * F + f] * (double)s_ref[f];
       for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
@@ -327,10 +332,11 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
   // chunks, then the norm part's hi-magnitude and lo-magnitude operands, then the
   // lane's reference magnitudes (bf16 pairs, in the order band_sq forms its bands)
   u32x4* dst = reinterpret_cast<u32x4*>(a.B) + ug * S::NBT * 64;
-  for (int q = first ? t : S::NBT * 64; q < S::NBT * 64; q += 256) {
+  for (int q = own_b ? t : S::NBT * 64; q < S::NBT * 64; q += 256) {
     const int s = q / 64, lane = q % 64;
     const int col = lane & 15, grp = lane >> 4;
     if (s >= NB) {
+      if (hz > 0) continue;   // the reference magnitudes: block 0
       u32x4 w4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -344,6 +350,7 @@ __global__ __launch_bounds__(256) void k_coef(CoefArgs a, Offsets offs) {
     bool lo = false;
     if (col < G) head = col;
     else if (col >= 8 && col < 8 + G) { head = col - 8; lo = true; }
+    if (hz >= 0 && head != hz && !(head < 0 && hz == 0)) continue;   // another block's head (zeros: block 0)
     u32x4 w4 = {0u, 0u, 0u, 0u};
     if (head >= 0) {
       if (s < S::NKC) {
@@ -2445,9 +2452,12 @@ hipError_t launch_coef(const CoefArgs& a, const Offsets& offs, hipStream_t s) {
   // the maximum over offsets writes nblk * d/32 * 64 operands per (unit, KV head):
   // with few pairs, they are shared out over up to nblk blocks per pair so that the
   // launch fills the device
+  // the mean over offsets with few pairs: one block per query head, so that each
+  // block's chain of dependent steps covers one head
   const long pairs = (long)a.n_units * a.hkv;
   int zs = 1;
   if (a.omax) zs = (int)std::max(1L, std::min<long>(a.ob.nblk, (1024 + pairs - 1) / pairs));
+  else if (pairs <= 64 && a.group > 1) zs = a.group;
   const dim3 grid((unsigned)a.n_units, (unsigned)a.hkv, (unsigned)zs);
 #define TRIA_COEF_CASE(DD, PP)                                                   \
   if (a.d == DD && a.pairing == PP) {                                           \
@@ -2477,10 +2487,37 @@ size_t score_lds(int d, int group, bool paged, int omax, int nblk, int tile, int
   return ((used + 3) & ~(size_t)3) * 4 + (blocks > (size_t)kBins * 4 ? blocks : (size_t)kBins * 4);
 }
 
+namespace {
+// Resident-capacity answers, kept per device: a pass asks up to three times per
+// tria_score call, and each answer costs an occupancy query and a device-attribute
+// query of host time, which a launch-bound pass (few, short kernels) pays in full.
+// An answer depends only on the device, the kernel variant and its LDS bytes.
+struct CapEntry {
+  int dev, d, pairing, paged, omax, single;
+  size_t lds;
+  int cap;
+};
+constexpr int kCapSlots = 32;
+std::mutex g_cap_mu;
+CapEntry g_cap[kCapSlots];
+int g_cap_used = 0, g_cap_next = 0;
+}  // namespace
+
 int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk, int tile, int block_size,
                    int single) {
   const size_t lds = score_lds(d, group, paged, omax, nblk, tile, block_size, single);
   int per_cu = 0, dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const CapEntry key{dev, d, pairing, paged ? 1 : 0, omax ? 1 : 0, !paged && !omax && single ? 1 : 0, lds, 0};
+  {
+    std::lock_guard<std::mutex> lock(g_cap_mu);
+    for (int i = 0; i < g_cap_used; ++i) {
+      const CapEntry& c = g_cap[i];
+      if (c.dev == key.dev && c.d == key.d && c.pairing == key.pairing && c.paged == key.paged &&
+          c.omax == key.omax && c.single == key.single && c.lds == key.lds)
+        return c.cap;
+    }
+  }
   hipError_t e = hipErrorInvalidValue;
 #define TRIA_OCC_CASE(DD, PP, PG, MX)                                                                     \
   if (d == DD && pairing == PP && paged == PG && (omax != 0) == MX)                                       \
@@ -2507,9 +2544,16 @@ int score_capacity(int d, int pairing, bool paged, int group, int omax, int nblk
 #undef TRIA_OCC_CASES
 #undef TRIA_OCC_CASE
   if (e != hipSuccess) return -1;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  return per_cu * cus;
+  CapEntry entry = key;
+  entry.cap = per_cu * cus;
+  {
+    std::lock_guard<std::mutex> lock(g_cap_mu);
+    g_cap[g_cap_next] = entry;
+    g_cap_next = (g_cap_next + 1) % kCapSlots;
+    if (g_cap_used < kCapSlots) ++g_cap_used;
+  }
+  return entry.cap;
 }
 
 hipError_t launch_score(const ScoreArgs& a, int d, int pairing, int max_wg, hipStream_t s) {
